@@ -1,0 +1,426 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test names what it pins: a value worked by hand from the pages' definitions, a
+workload count, a closed form, a library routine, or a brute-force formulation written
+separately from the oracle's key-list code.  A plausible mistake in the oracle (a
+dropped sink, an off-by-one window, a wrong slot count, a sign or scale error in the
+softmax, a transposed projection, a mis-aligned causal mask) fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import masw_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Eq. 2: hand-worked example, closed forms, library routine
+# ---------------------------------------------------------------------------
+
+def test_eq2_hand_example():
+    g = _load("eq2_hand_example.json")
+    q = np.array([math.sqrt(2.0) * math.log(2.0), 0.0])
+    K = np.array(g["K"])
+    V = np.array(g["V"])
+    scale = O.default_scale(g["head_dim"])
+    np.testing.assert_allclose(O.softmax_weights(q, K, scale), g["weights"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.attend(q, K, V, scale), g["out"], rtol=0, atol=1e-13)
+
+
+def test_attend_closed_forms():
+    rng = np.random.default_rng(0)
+    D = 16
+    K = rng.normal(size=(9, D))
+    V = rng.normal(size=(9, D))
+    q = rng.normal(size=D)
+    s = 0.3
+    # a single key returns its value exactly
+    np.testing.assert_array_equal(O.attend(q, K[:1], V[:1], s), V[0])
+    # a zero query averages the values
+    np.testing.assert_allclose(O.attend(np.zeros(D), K, V, s), V.mean(axis=0), atol=1e-15)
+    # constant values are reproduced
+    np.testing.assert_allclose(O.attend(q, K, np.full((9, D), 2.5), s), np.full(D, 2.5), atol=1e-14)
+    # weights form a probability row
+    w = O.softmax_weights(q, K, s)
+    assert abs(w.sum() - 1.0) < 1e-12 and (w > 0).all()
+    # a larger score gets a larger weight (sign of the exponent)
+    assert np.argmax(w) == np.argmax(K @ q)
+    # permuting keys and values together changes nothing
+    perm = rng.permutation(9)
+    np.testing.assert_allclose(O.attend(q, K[perm], V[perm], s), O.attend(q, K, V, s), atol=1e-14)
+    # shifting every key along q shifts every score equally: output unchanged
+    K2 = K + 3.0 * q[None, :] / np.dot(q, q)
+    np.testing.assert_allclose(O.attend(q, K2, V, s), O.attend(q, K, V, s), atol=1e-13)
+    # huge scores do not overflow (max subtraction)
+    out = O.attend(q * 1e4, K, V, s)
+    assert np.isfinite(out).all()
+    np.testing.assert_allclose(out, V[np.argmax(K @ q)], atol=1e-9)
+
+
+def test_two_key_ratio_closed_form():
+    # scores differing by ln 3 give weights 3/4 and 1/4
+    D = 4
+    scale = O.default_scale(D)
+    q = np.array([math.log(3.0) / scale, 0, 0, 0])
+    K = np.array([[1.0, 0, 0, 0], [0.0, 1, 0, 0]])
+    V = np.array([[4.0, 0, 0, 0], [0.0, 4, 0, 0]])
+    np.testing.assert_allclose(O.attend(q, K, V, scale), [3.0, 1.0, 0, 0], atol=1e-14)
+
+
+def test_gqa_attend_matches_torch_sdpa():
+    rng = np.random.default_rng(1)
+    Hq, Hkv, n, D = 6, 2, 37, 32
+    q = rng.normal(size=(Hq, D))
+    K = rng.normal(size=(Hkv, n, D))
+    V = rng.normal(size=(Hkv, n, D))
+    scale = O.default_scale(D)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None, :],
+        torch.from_numpy(K).repeat_interleave(Hq // Hkv, dim=0),
+        torch.from_numpy(V).repeat_interleave(Hq // Hkv, dim=0),
+        scale=scale)[:, 0, :].numpy()
+    np.testing.assert_allclose(O.gqa_attend(q, K, V, scale), ref, atol=1e-13)
+    # the grouping is contiguous: head h reads KV head h // G, not h % Hkv
+    wrong = O.gqa_attend(q, K[[1, 0]], V[[1, 0]], scale)
+    assert np.abs(wrong - ref).max() > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Eq. 4: key lists, counts, invariants
+# ---------------------------------------------------------------------------
+
+def test_window_hand_example():
+    g = _load("window_hand_example.json")
+    S, W, r = g["S"], g["W"], g["r"]
+    for c in g["cases"]:
+        keys = O.keylist(c["t"], S, W, r)
+        assert [i for k, i in keys if k == "raw"] == c["raw"], c
+        assert [m for k, m in keys if k == "slot"] == c["slots"], c
+        # sinks come first, then the window ascending, then slots ascending
+        assert keys == [("raw", i) for i in c["raw"]] + [("slot", m) for m in c["slots"]]
+
+
+def test_tiny_workload_counts():
+    g = _load("memory_counts.json")["tiny_workload"]
+    S, W, r, t = g["S"], g["W"], g["r"], g["t"]
+    assert O.visible_slot_count(t, S, W, r) == g["slots"]
+    crossed = [u for u in range(t + 1, t + g["next_steps"] + 1) if O.is_boundary(u, S, W, r)]
+    assert len(crossed) == g["boundaries_crossed"]
+    # a literal floor(t / r) count would give 12 here, a ceiling 11
+    assert t // r != g["slots"] and -(-(t - S - W) // r) != g["slots"]
+
+
+def test_slot_query_count_3b():
+    g = _load("memory_counts.json")["slot_query_3b"]
+    S, W, r = g["S"], g["W"], g["r"]
+    for prior in g["prior_slots"]:
+        m = prior + 1
+        keys = O.slot_query_keylist(m, S, W, r)
+        assert len(keys) == S + W + prior
+        assert sum(1 for k, _ in keys if k == "slot") == prior
+        # the window of the slot query starts at the first token of the block g_m compresses
+        raw = [i for k, i in keys if k == "raw" and i > S]
+        assert raw[0] == O.block_positions(m, S, r)[0] and len(raw) == W
+
+
+def test_worked_example_divergence_is_documented():
+    g = _load("memory_counts.json")["worked_example_page"]
+    S, W, r, t = g["S"], g["W"], g["r"], g["t"]
+    n = O.visible_slot_count(t, S, W, r)
+    keys = O.keylist(t, S, W, r)
+    assert O.is_boundary(t, S, W, r) == n      # t = 4100 is a boundary under the reading
+    assert (n, len(keys)) == (961, 1217)
+    assert n != g["page_slots_approx"] and len(keys) != g["page_entries"]
+    # the page's 8-token window contradicts Eq. 4 with W = 128
+    assert len(O.local_positions(t, S, W)) == W != g["page_local"]
+
+
+def _invariant_grid():
+    for S in (0, 1, 4, 7):
+        for W in (1, 3, 8, 32):
+            for r in (1, 2, 5, 16, 32):
+                if r <= W:
+                    yield S, W, r
+
+
+@pytest.mark.parametrize("S,W,r", list(_invariant_grid()))
+def test_keylist_invariants(S, W, r):
+    C = O.ring_capacity(W, r)
+    for t in range(1, S + W + 6 * r + 3):
+        keys = O.keylist(t, S, W, r)
+        n = O.visible_slot_count(t, S, W, r)
+        raw = [i for k, i in keys if k == "raw"]
+        slots = [m for k, m in keys if k == "slot"]
+        # I1 exact size; I2 the page's working-set bound
+        assert len(keys) == min(t, S) + min(max(t - S, 0), W) + n
+        assert len(keys) <= S + W + t // r
+        # I3 local part by enumeration straight from Eq. 4
+        local = [i for i in range(1, t + 1) if i > S and max(S + 1, t - W + 1) <= i <= t]
+        assert raw == list(range(1, min(S, t) + 1)) + local
+        assert len(set(raw)) == len(raw)
+        # I4 no slot while t <= S + W: the memory is the whole prefix
+        if t <= S + W:
+            assert raw == list(range(1, t + 1)) and not slots
+        # I7 no visible raw token lies in a block whose slot is visible
+        for m in slots:
+            assert not set(O.block_positions(m, S, r)) & set(raw)
+        # every non-sink raw token older than the window has left it for good:
+        # its block's slot is visible, or the block is still waiting (< r steps)
+        for i in range(S + 1, t + 1):
+            if i not in raw:
+                m = -(-(i - S) // r)
+                assert m in slots or O.boundary_step(m, S, W, r) > t
+                assert O.boundary_step(m, S, W, r) - t < r
+        # the ring keeps every visible raw token
+        assert t - C < (local[0] if local else t + 1)
+    # I6 the slot query sees exactly what the decode query saw r steps before
+    for m in range(1, 6):
+        assert O.slot_query_keylist(m, S, W, r) == O.keylist(S + W + (m - 1) * r, S, W, r)
+
+
+@settings(max_examples=200, deadline=None)
+@given(S=st.integers(0, 9), W=st.integers(1, 40), r=st.integers(1, 40), t=st.integers(1, 400))
+def test_keylist_property(S, W, r, t):
+    if r > W:
+        return
+    keys = O.keylist(t, S, W, r)
+    n = O.visible_slot_count(t, S, W, r)
+    assert len(keys) == min(t, S) + min(max(t - S, 0), W) + n
+    assert len(keys) <= S + W + t // r
+    # slots appear exactly at the boundary steps
+    assert n == sum(1 for u in range(1, t + 1) if O.is_boundary(u, S, W, r))
+
+
+# ---------------------------------------------------------------------------
+# Ring placement and append legality (bookkeeping behind the key list)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,W,r", [(0, 1, 1), (4, 32, 16), (2, 3, 2), (7, 8, 5), (1, 5, 5)])
+def test_ring_closed_form_vs_fifo_simulation(S, W, r):
+    """A literal FIFO of C cells: the next free cell advances by one per non-sink token."""
+    C = O.ring_capacity(W, r)
+    cells = [None] * C
+    nxt = 0
+    for t in range(1, S + 4 * C + 3):
+        if t > S:
+            cells[nxt] = t
+            nxt = (nxt + 1) % C
+            assert O.ring_cell(t, S, W, r) == (nxt - 1) % C
+        assert O.expected_ring(t, S, W, r) == cells
+        # every visible raw non-sink token is resident in the ring
+        held = set(c for c in cells if c is not None)
+        for kind, i in O.keylist(t, S, W, r):
+            if kind == "raw" and i > S:
+                assert i in held
+        # at a boundary the slot query's window is resident as well
+        m = O.is_boundary(t, S, W, r)
+        if m:
+            for kind, i in O.slot_query_keylist(m, S, W, r):
+                if kind == "raw" and i > S:
+                    assert i in held
+
+
+@pytest.mark.parametrize("S,W,r", [(4, 32, 16), (0, 3, 3), (2, 3, 2), (5, 9, 4)])
+def test_append_legality_schedule(S, W, r):
+    """Materializing at every boundary keeps every append legal; skipping one slot makes
+    exactly the first append that would overwrite its block illegal, at t_m + 1."""
+    n_slots = 0
+    for i in range(1, S + W + 8 * r):
+        assert O.append_is_legal(i, n_slots, S, W, r)
+        if O.is_boundary(i, S, W, r):
+            n_slots += 1
+    for m in (1, 2, 3):
+        tm = O.boundary_step(m, S, W, r)
+        assert O.append_is_legal(tm, m - 1, S, W, r)
+        assert not O.append_is_legal(tm + 1, m - 1, S, W, r)
+        assert O.append_is_legal(tm + 1, m, S, W, r)
+
+
+def test_ring_capacity_is_tight():
+    """With one cell fewer than W + r the slot query's window is no longer resident."""
+    S, W, r = 4, 32, 16
+    C = O.ring_capacity(W, r) - 1
+    m = 3
+    tm = O.boundary_step(m, S, W, r)
+    window = [i for k, i in O.slot_query_keylist(m, S, W, r) if k == "raw" and i > S]
+    assert window[0] <= tm - C     # the oldest token would already be overwritten
+
+
+# ---------------------------------------------------------------------------
+# Brute force: dense masks over every entry ever created vs the key-list oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,W,r", [(4, 32, 16), (0, 5, 2), (3, 4, 4), (2, 6, 1), (1, 8, 3)])
+def test_dense_mask_bruteforce(S, W, r):
+    rng = np.random.default_rng(7)
+    D, Hkv, hidden = 8, 2, 8
+    G = 2
+    T = S + W + 5 * r + 3
+    raw_k = rng.normal(size=(T, Hkv, D))
+    raw_v = rng.normal(size=(T, Hkv, D))
+    wk = rng.normal(size=(hidden, Hkv * D)) / 3
+    wv = rng.normal(size=(hidden, Hkv * D)) / 3
+    scale = O.default_scale(D)
+    mem = O.DraftMemory(S, W, r, Hkv, D, bf16_cache=False)
+    slot_k, slot_v = [], []
+    for t in range(1, T + 1):
+        mem.append(raw_k[t - 1:t], raw_v[t - 1:t])
+        m = mem.pending_boundary()
+        if m:
+            h = rng.normal(size=hidden)
+            qg = rng.normal(size=(Hkv * G, D))
+            og = mem.materialize(h, wk, wv, qg, scale)
+            kg, vg = mem.slots[m]
+            slot_k.append(kg)
+            slot_v.append(vg)
+            sk, sv = np.stack(slot_k), np.stack(slot_v)
+            for hq in range(Hkv * G):
+                ref = O.dense_mask_slot_query(qg[hq], raw_k[:t, hq // G], raw_v[:t, hq // G],
+                                              sk[:, hq // G], sv[:, hq // G], m, S, W, r, scale)
+                np.testing.assert_allclose(og[hq], ref, atol=1e-12)
+        q = rng.normal(size=(Hkv * G, D))
+        out = mem.decode(q, scale)
+        sk = np.stack(slot_k) if slot_k else np.zeros((0, Hkv, D))
+        sv = np.stack(slot_v) if slot_v else np.zeros((0, Hkv, D))
+        for hq in range(Hkv * G):
+            ref = O.dense_mask_decode(q[hq], raw_k[:t, hq // G], raw_v[:t, hq // G],
+                                      sk[:, hq // G], sv[:, hq // G], t, S, W, r, scale)
+            np.testing.assert_allclose(out[hq], ref, atol=1e-12)
+        # I4: full attention while t <= S + W, bitwise (same keys, same order, same fp64 ops)
+        if t <= S + W:
+            full = O.fullkv_decode(q, raw_k[:t].transpose(1, 0, 2), raw_v[:t].transpose(1, 0, 2), t, scale)
+            np.testing.assert_array_equal(out, full)
+
+
+def test_include_self_bruteforce():
+    rng = np.random.default_rng(3)
+    S, W, r, D, Hkv, hidden = 2, 6, 3, 8, 1, 8
+    T = S + W + 4 * r
+    raw_k = rng.normal(size=(T, Hkv, D))
+    raw_v = rng.normal(size=(T, Hkv, D))
+    wk = rng.normal(size=(hidden, D))
+    wv = rng.normal(size=(hidden, D))
+    scale = O.default_scale(D)
+    mem = O.DraftMemory(S, W, r, Hkv, D, bf16_cache=False)
+    sk, sv = [], []
+    for t in range(1, T + 1):
+        mem.append(raw_k[t - 1:t], raw_v[t - 1:t])
+        m = mem.pending_boundary()
+        if m:
+            qg = rng.normal(size=(1, D))
+            og = mem.materialize(rng.normal(size=hidden), wk, wv, qg, scale, include_self=True)
+            sk.append(mem.slots[m][0])
+            sv.append(mem.slots[m][1])
+            ref = O.dense_mask_slot_query(qg[0], raw_k[:t, 0], raw_v[:t, 0], np.stack(sk)[:, 0],
+                                          np.stack(sv)[:, 0], m, S, W, r, scale, include_self=True)
+            np.testing.assert_allclose(og[0], ref, atol=1e-12)
+            assert len(O.slot_query_keylist(m, S, W, r, True)) == len(O.slot_query_keylist(m, S, W, r)) + 1
+
+
+def test_one_hot_values_expose_the_support():
+    """V of entry j = e_j: the output is the probability row, so it shows exactly which
+    entries carry mass.  Excluded or evicted entries must carry none."""
+    S, W, r, D = 4, 32, 16, 64
+    rng = np.random.default_rng(11)
+    mem = O.DraftMemory(S, W, r, 1, D, bf16_cache=False)
+    T = 200
+    K = rng.normal(size=(T, 1, D))
+    for t in range(1, T + 1):
+        mem.append(K[t - 1:t], np.zeros((1, 1, D)))
+        if mem.pending_boundary():
+            mem.materialize(rng.normal(size=D), np.eye(D), np.eye(D), rng.normal(size=(1, D)), 0.125)
+    keys = O.keylist(T, S, W, r)
+    assert len(keys) <= D
+    for j, (kind, idx) in enumerate(keys):   # overwrite V of the visible entries by e_j
+        e = np.zeros((1, D))
+        e[0, j] = 1
+        if kind == "raw":
+            mem.raw[idx] = (mem.raw[idx][0], e)
+        else:
+            mem.slots[idx] = (mem.slots[idx][0], e)
+    q = rng.normal(size=(1, D))
+    out = mem.decode(q, 0.125)[0]
+    assert abs(out.sum() - 1.0) < 1e-12
+    assert (out[len(keys):] == 0).all()
+    np.testing.assert_allclose(out[:len(keys)], mem.decode_weights(q[0], 0, 0.125), atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Mirrored projection and bf16 rounding
+# ---------------------------------------------------------------------------
+
+def test_projection_orientation_and_heads():
+    rng = np.random.default_rng(5)
+    hidden, Hkv, D = 12, 3, 4
+    wk = rng.normal(size=(hidden, Hkv * D))
+    wv = rng.normal(size=(hidden, Hkv * D))
+    for i in range(hidden):
+        e = np.zeros(hidden)
+        e[i] = 1.0
+        kg, vg = O.project_slot(e, wk, wv, Hkv, D, bf16_cache=False)
+        # a one-hot hidden state selects row i of the weights; head k is column block k
+        np.testing.assert_array_equal(kg, wk[i].reshape(Hkv, D))
+        np.testing.assert_array_equal(vg, wv[i].reshape(Hkv, D))
+    # copy-initialized mirrored weights reproduce the backbone's own key (library matmul)
+    h = rng.normal(size=hidden)
+    kg, _ = O.project_slot(h, wk, wv, Hkv, D, bf16_cache=False)
+    ref = (torch.from_numpy(h)[None] @ torch.from_numpy(wk))[0].numpy().reshape(Hkv, D)
+    np.testing.assert_allclose(kg, ref, atol=1e-12)
+
+
+def test_to_bf16_matches_torch_and_ties():
+    x = torch.randn(20000, dtype=torch.float32) * torch.logspace(-30, 30, 20000)
+    ref = x.to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.to_bf16(x.double().numpy()), ref)
+    # exact ties round to the even neighbour
+    assert O.to_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert O.to_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert O.to_bf16(-(1.0 + 2.0 ** -8)) == -1.0
+    # just above a tie rounds up; fp64 inputs are rounded once, not through fp32
+    assert O.to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 1.0 + 2.0 ** -7
+    # subnormal range and overflow
+    assert O.to_bf16(2.0 ** -133) == 2.0 ** -133
+    assert O.to_bf16(1.5 * 2.0 ** -134) == 2.0 ** -133
+    assert O.to_bf16(3.0e38) == float(torch.tensor(3.0e38).to(torch.bfloat16))
+    assert O.to_bf16(3.4e38) == np.inf and O.to_bf16(0.0) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Full-KV decode and verifier
+# ---------------------------------------------------------------------------
+
+def test_verify_matches_torch_masked_sdpa():
+    rng = np.random.default_rng(9)
+    n_q, Hq, Hkv, N, D = 6, 8, 2, 50, 16
+    t = 45
+    q = rng.normal(size=(n_q, Hq, D))
+    K = rng.normal(size=(Hkv, N, D))
+    V = rng.normal(size=(Hkv, N, D))
+    scale = O.default_scale(D)
+    out = O.fullkv_verify(q, K, V, t, scale)
+    # explicit boolean mask: query j may see key rows 0 .. t - n_q + j (bottom-right aligned)
+    mask = np.zeros((n_q, t), dtype=bool)
+    for j in range(n_q):
+        mask[j, : t - n_q + 1 + j] = True
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).permute(1, 0, 2)                       # [Hq][n_q][D]
+    kt = torch.from_numpy(K[:, :t]).repeat_interleave(G, 0)
+    vt = torch.from_numpy(V[:, :t]).repeat_interleave(G, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=scale).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, atol=1e-13)
+    # the last query sees every key, the first sees n_q - 1 fewer
+    np.testing.assert_allclose(out[-1], O.fullkv_decode(q[-1], K, V, t, scale), atol=0)
+    np.testing.assert_allclose(out[0], O.fullkv_decode(q[0], K, V, t - n_q + 1, scale), atol=0)

@@ -1,0 +1,348 @@
+"""Benchmark: MASW draft decode attention vs the full-KV draft baseline on one MI355X.
+
+Workload: Llama-3.2-3B-shaped draft attention stack (28 layers, 24 query heads, 8 KV
+heads, head_dim 128, bf16), batch 8, S=4 sinks, W=2048 local window, r=64 slot
+interval; seeded synthetic N(0,1) K/V/q, slots pre-materialized as the bf16 projection
+of seeded hidden states through seeded mirrored weights.
+
+One step = one decode position for all 8 sequences through all 28 layers: per layer
+raw append (with eviction), slot materialization when the step is a slot boundary
+(mirrored projection + structured-mask slot query + slot append), and the draft
+attention over sink ++ window ++ slots.  The headline value is MASW steps/s at prefix
+32768; the same line carries the prefix sweep 1K..32K for MASW and for the full-KV
+baseline (same kernel over the whole cache), the roofline of the decode attention
+kernel and the fp64 oracle timed on the host cores.
+
+Steps are captured once into HIP graphs (one for ordinary steps, one for boundary
+steps) and replayed; the host picks the graph from its own position counter, so no
+device value is read inside the timed region.
+
+    python bench.py [--gpus 1] [--steps 256] [--warmup 16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import draft_kv_attention_amd as M   # noqa: E402
+import seeded_inputs as SI           # noqa: E402
+
+METRIC = "draft attn steps/s + HBM GB/s (% peak) vs prefix 1K-32K, MASW vs full-KV"
+HBM_PEAK_GBS = 8000.0
+SHAPE = SI.SWEEP_3B
+T_HEAD = 32768
+
+
+def n_slots_at(t, S, W, r):
+    return max(0, t - S - W) // r
+
+
+def keys_at(t, S, W, r):
+    return min(t, S) + min(max(t - S, 0), W) + n_slots_at(t, S, W, r)
+
+
+def is_boundary(t, S, W, r):
+    d = t - S - W
+    return d >= r and d % r == 0
+
+
+class Stack:
+    """28 layers of MASW memory plus the full caches, inputs and graphs."""
+
+    def __init__(self, shape, t_max, dev, seed=0, with_full=True):
+        self.shape = shape
+        S, W, r = shape.sink, shape.window, shape.interval
+        self.S, self.W, self.r = S, W, r
+        self.L = shape.layers
+        self.dev = dev
+        self.max_slots = n_slots_at(t_max, S, W, r) + 2
+        self.d = M.Dims(batch=shape.batch, n_q_heads=shape.n_q_heads, n_kv_heads=shape.n_kv_heads,
+                        head_dim=shape.head_dim, sink=S, window=W, interval=r,
+                        max_slots=self.max_slots, dtype=shape.dtype)
+        B, Hq, Hkv, D, hid = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.hidden
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+
+        def rnd(*s, std=1.0):
+            return (torch.randn(*s, generator=g, device=dev, dtype=torch.float32) * std).to(shape.dtype)
+
+        self.layers, self.wk, self.wv = [], [], []
+        for _ in range(self.L):
+            lay = M.alloc_layer(self.d, dev, fill=None)
+            lay.k_sink.copy_(rnd(*lay.k_sink.shape)); lay.v_sink.copy_(rnd(*lay.v_sink.shape))
+            lay.k_ring.copy_(rnd(*lay.k_ring.shape)); lay.v_ring.copy_(rnd(*lay.v_ring.shape))
+            wk, wv = rnd(hid, Hkv * D, std=shape.w_std), rnd(hid, Hkv * D, std=shape.w_std)
+            hs = rnd(B * self.max_slots, hid)
+            lay.k_slot.copy_((hs @ wk).view(B, self.max_slots, Hkv, D).permute(0, 2, 1, 3))
+            lay.v_slot.copy_((hs @ wv).view(B, self.max_slots, Hkv, D).permute(0, 2, 1, 3))
+            self.layers.append(lay)
+            self.wk.append(wk)
+            self.wv.append(wv)
+        self.seq = M.alloc_seq(B, dev)
+        self.ws = M.workspace(self.d, M.OP_MATERIALIZE, device=dev)
+        self.k_new = [rnd(B, 1, Hkv, D) for _ in range(self.L)]
+        self.v_new = [rnd(B, 1, Hkv, D) for _ in range(self.L)]
+        self.q = [rnd(B, Hq, D) for _ in range(self.L)]
+        self.out = [torch.empty(B, Hq, D, dtype=shape.dtype, device=dev) for _ in range(self.L)]
+        self.h = [rnd(B, hid) for _ in range(self.L)]
+        self.qg = [rnd(B, Hq, D) for _ in range(self.L)]
+        self.og = [torch.empty(B, Hq, D, dtype=shape.dtype, device=dev) for _ in range(self.L)]
+        self.full_len = t_max + 8
+        self.kf, self.vf = [], []
+        if with_full:
+            for _ in range(self.L):
+                self.kf.append(rnd(B, Hkv, self.full_len, D))
+                self.vf.append(rnd(B, Hkv, self.full_len, D))
+            self.fd = M.Dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, dtype=shape.dtype)
+            self.seq_full = torch.zeros(B, dtype=torch.int32, device=dev)
+            self.err_full = torch.zeros(1, dtype=torch.int32, device=dev)
+            self.ws_full = M.workspace(self.fd, M.OP_FULLKV_DECODE, max_keys=self.full_len, device=dev)
+        self.graphs = {}
+
+    # -- state -------------------------------------------------------------
+    def set_position(self, t):
+        self.seq.seq_len.fill_(t)
+        n = n_slots_at(t, self.S, self.W, self.r)
+        for lay in self.layers:
+            lay.n_slots.fill_(n)
+        if self.kf:
+            self.seq_full.fill_(t)
+        self.t = t
+
+    # -- one step ----------------------------------------------------------
+    def masw_step(self, boundary):
+        self.seq.seq_len.add_(1)
+        for l in range(self.L):
+            lay = self.layers[l]
+            M.masw_evict_append(self.d, lay, self.seq, self.k_new[l], self.v_new[l])
+            if boundary:
+                M.masw_materialize_slot(self.d, lay, self.seq, self.h[l], self.wk[l], self.wv[l],
+                                        self.qg[l], self.og[l], self.ws)
+            M.masw_draft_attn(self.d, lay, self.seq, self.q[l], self.out[l], self.ws)
+
+    def full_step(self):
+        self.seq_full.add_(1)
+        for l in range(self.L):
+            M.fullkv_append(self.fd, self.kf[l], self.vf[l], self.seq_full, self.err_full,
+                            self.k_new[l], self.v_new[l])
+            M.fullkv_decode_attn(self.fd, self.kf[l], self.vf[l], self.seq_full, self.err_full,
+                                 self.q[l], self.out[l], self.ws_full)
+
+    def capture(self):
+        """Capture the three step variants; each capture advances nothing (state is reset)."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for name, fn in (("masw", lambda: self.masw_step(False)),
+                             ("masw_boundary", lambda: self.masw_step(True)),
+                             ("full", self.full_step if self.kf else None)):
+                if fn is None:
+                    continue
+                fn()   # warm once eagerly on the side stream
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    fn()
+                self.graphs[name] = g
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+
+    def replay_masw(self):
+        nxt = self.t + 1
+        self.graphs["masw_boundary" if is_boundary(nxt, self.S, self.W, self.r) else "masw"].replay()
+        self.t = nxt
+
+    def replay_full(self):
+        self.graphs["full"].replay()
+        self.t += 1
+
+    # -- algorithmic bytes ---------------------------------------------------
+    def kv_row_bytes(self):
+        sh = self.shape
+        return sh.n_kv_heads * sh.head_dim * 2 * 2          # K and V, bf16
+
+    def attn_bytes(self, keys):
+        sh = self.shape
+        return sh.batch * (keys * self.kv_row_bytes() + 2 * sh.n_q_heads * sh.head_dim * 2)
+
+    def masw_step_bytes(self, t):
+        sh = self.shape
+        b = self.L * (self.attn_bytes(keys_at(t, self.S, self.W, self.r)) + sh.batch * self.kv_row_bytes())
+        if is_boundary(t, self.S, self.W, self.r):
+            m = (t - self.S - self.W) // self.r
+            proj = 2 * sh.hidden * sh.n_kv_heads * sh.head_dim * 2 + sh.batch * sh.hidden * 2
+            b += self.L * (proj + self.attn_bytes(self.S + self.W + m - 1) + sh.batch * self.kv_row_bytes())
+        return b
+
+    def full_step_bytes(self, t):
+        return self.L * (self.attn_bytes(t) + self.shape.batch * self.kv_row_bytes())
+
+
+def time_steps(stack, which, t_start, warmup, steps):
+    """Replay `steps` graph steps from position t_start after `warmup` untimed ones."""
+    stack.set_position(t_start)
+    rep = stack.replay_masw if which == "masw" else stack.replay_full
+    for _ in range(warmup):
+        rep()
+    t0 = stack.t
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        rep()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    bytes_fn = stack.masw_step_bytes if which == "masw" else stack.full_step_bytes
+    avg_bytes = sum(bytes_fn(t) for t in range(t0 + 1, t0 + steps + 1)) / steps
+    return ms, avg_bytes
+
+
+def kernel_roofline(stack, t, reps=4):
+    """Average duration of one masw_draft_attn call, from events around each call.
+
+    A spin kernel first gives the host a head start, so every call is already queued
+    when the GPU reaches it and each event pair brackets only the call's own kernels.
+    """
+    stack.set_position(t)
+    evs = []
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.05))
+    for _ in range(reps):
+        for l in range(stack.L):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            M.masw_draft_attn(stack.d, stack.layers[l], stack.seq, stack.q[l], stack.out[l], stack.ws)
+            b.record()
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)   # us
+    avg_us = float(np.mean(durs))
+    nbytes = stack.attn_bytes(keys_at(t, stack.S, stack.W, stack.r))
+    achieved = nbytes / (avg_us * 1e-6) / 1e9
+    return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                kernel="masw_draft_attn", avg_us=round(avg_us, 2),
+                median_us=round(float(np.median(durs)), 2), bytes_per_launch=int(nbytes),
+                prefix=t, launches=len(durs))
+
+
+def cpu_baseline(budget_s=15.0):
+    """The fp64 oracle's decode over the same memory shape, on the host, single thread.
+
+    Sample: (layer, sequence) units of the 3B-shaped MASW decode at prefix 32768 (one
+    query per q head over keylist(t)), repeated until ~budget_s; scaled to steps/s of
+    the 28-layer, 8-sequence step.
+    """
+    from threadpoolctl import threadpool_limits
+    from oracle import masw_oracle as O
+    sh = SHAPE
+    S, W, r, Hkv, D = sh.sink, sh.window, sh.interval, sh.n_kv_heads, sh.head_dim
+    t = T_HEAD
+    rng = np.random.default_rng(0)
+    n = O.visible_slot_count(t, S, W, r)
+    raw_k = rng.standard_normal((t + 1, Hkv, D), dtype=np.float32)
+    raw_v = rng.standard_normal((t + 1, Hkv, D), dtype=np.float32)
+    slot_k = rng.standard_normal((n + 1, Hkv, D), dtype=np.float32)
+    slot_v = rng.standard_normal((n + 1, Hkv, D), dtype=np.float32)
+    scale = O.default_scale(D)
+    units = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            keys = O.keylist(t, S, W, r)
+            ks = np.stack([raw_k[i] if kind == "raw" else slot_k[i] for kind, i in keys], axis=1)
+            vs = np.stack([raw_v[i] if kind == "raw" else slot_v[i] for kind, i in keys], axis=1)
+            q = rng.standard_normal((sh.n_q_heads, D))
+            O.gqa_attend(q, ks.astype(np.float64), vs.astype(np.float64), scale)
+            units += 1
+        el = time.perf_counter() - t0
+    per_step = el / units * sh.layers * sh.batch
+    return dict(value=round(1.0 / per_step, 5), unit="steps/s", cores=1, kind="oracle",
+                sample=f"{units} (layer, sequence) MASW decode units at prefix {t} "
+                       f"({len(O.keylist(t, S, W, r))} keys, 24 q heads) in {el:.1f} s, "
+                       f"scaled x{sh.layers * sh.batch} to one 28-layer batch-8 step")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--sweep-steps", type=int, default=48)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the draft path shards by sequence or KV head "
+              "without communication, so a multi-GPU figure is not produced", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    M.lib()
+    sh = SHAPE
+    t_max = T_HEAD + args.warmup + args.steps + 8
+    if not args.no_sweep:
+        t_max = max(t_max, max(SI.SWEEP_PREFIXES) + args.sweep_steps + 40)
+    print(f"[bench] allocating 28-layer stack, prefix up to {t_max}", file=sys.stderr, flush=True)
+    stack = Stack(sh, t_max, dev)
+    stack.capture()
+    print("[bench] graphs captured", file=sys.stderr, flush=True)
+
+    # headline: MASW at prefix 32768
+    ms, nbytes = time_steps(stack, "masw", T_HEAD, args.warmup, args.steps)
+    value = 1e3 / ms
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(f"[bench] MASW t={T_HEAD}: {ms:.3f} ms/step {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+
+    sweep = []
+    if not args.no_sweep:
+        for t in SI.SWEEP_PREFIXES:
+            row = dict(prefix=t, keys_masw=keys_at(t, sh.sink, sh.window, sh.interval), keys_full=t)
+            for which in ("masw", "full"):
+                m_s, b_s = time_steps(stack, which, t, 4, args.sweep_steps)
+                row[f"{which}_ms"] = round(m_s, 4)
+                row[f"{which}_steps_per_s"] = round(1e3 / m_s, 2)
+                row[f"{which}_gbs"] = round(b_s / (m_s * 1e-3) / 1e9, 1)
+                row[f"{which}_pct_peak"] = round(100 * b_s / (m_s * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)
+            sweep.append(row)
+            print(f"[bench] sweep t={t}: masw {row['masw_ms']} ms ({row['masw_gbs']} GB/s), "
+                  f"full {row['full_ms']} ms ({row['full_gbs']} GB/s)", file=sys.stderr, flush=True)
+
+    roof = kernel_roofline(stack, T_HEAD)
+    print(f"[bench] roofline {roof}", file=sys.stderr, flush=True)
+    err_bits = int(stack.seq.err.item()) | int(stack.err_full.item())
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline()
+        print(f"[bench] cpu baseline {cpu}", file=sys.stderr, flush=True)
+
+    full_head = next((r for r in sweep if r["prefix"] == T_HEAD), None)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "masw_draft_decode_llama3b_28L_b8_prefix32768", "layers": sh.layers,
+                   "batch": sh.batch, "prefix": T_HEAD, "q_heads": sh.n_q_heads,
+                   "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "sink": sh.sink,
+                   "window": sh.window, "interval": sh.interval},
+        "hbm_gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+        "tokens_per_s": round(value * sh.batch, 1),
+        "fullkv_at_prefix": full_head, "sweep": sweep, "device_err_bits": err_bits,
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

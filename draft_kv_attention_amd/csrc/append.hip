@@ -1,0 +1,72 @@
+// append.hip - raw-token append with implicit eviction (Technical Review §3.2,
+// Algorithm 1 step 5; §3.1 Eq. 4 local bullet).
+//
+// Position i <= S lands in sink row i-1; i > S in ring row (i-S-1) mod (W+r).  The
+// ring keeps W + r rows because a block leaves the W-window r-1 steps before its slot
+// is materialized and the slot query still reads it; overwriting a row therefore
+// evicts the token i-(W+r), which is legal only once that token's block has its slot.
+// Each thread moves one 16-byte packet of K and of V; all packets of one token take
+// the same decision, so an illegal token is skipped whole.
+#include "masw_internal.hpp"
+
+namespace masw {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+  constexpr int VEC = 16 / int(sizeof(T));
+  const int b = blockIdx.y;
+  const int per_tok = a.Hkv * a.D;
+  const int packets = a.n_new * per_tok / VEC;
+  const int t = a.seq_len[b];
+  if (t < a.n_new || (a.max_len > 0 && t > a.max_len)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SEQ_RANGE);
+    return;
+  }
+  int bits = 0;
+  for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < packets; p += gridDim.x * blockDim.x) {
+    const int e = p * VEC;
+    const int j = e / per_tok;
+    const int rem = e - j * per_tok;
+    const int kvh = rem / a.D;
+    const int d = rem - kvh * a.D;
+    const int i = t - a.n_new + 1 + j;
+    const size_t unit = size_t(b) * a.Hkv + kvh;
+    T* dk;
+    T* dv;
+    size_t off;
+    if (i <= a.g.S) {
+      off = (unit * a.sink_cap + (i - 1)) * a.D + d;
+      dk = static_cast<T*>(a.k_sink);
+      dv = static_cast<T*>(a.v_sink);
+    } else {
+      const int prev = i - a.g.C;   // the token this row held before
+      if (prev > a.g.S && a.n_slots[b] < (prev - a.g.S + a.g.r - 1) / a.g.r) {
+        bits |= MASW_DEV_PENDING_SLOT;
+        continue;
+      }
+      off = (unit * a.g.C + (i - a.g.S - 1) % a.g.C) * a.D + d;
+      dk = static_cast<T*>(a.k_ring);
+      dv = static_cast<T*>(a.v_ring);
+    }
+    const size_t src = ((size_t(b) * a.n_new + j) * a.Hkv + kvh) * a.D + d;
+    *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_new) + src);
+    *reinterpret_cast<uint4*>(dv + off) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_new) + src);
+  }
+  if (bits) atomicOr(a.err, bits);
+}
+
+}  // namespace
+
+int launch_append(const AppendArgs& a, int dtype, hipStream_t s) {
+  const int vec = dtype == MASW_BF16 ? 8 : 4;
+  const long packets = long(a.n_new) * a.Hkv * a.D / vec;
+  const int blocks = int(std::min<long>((packets + 255) / 256, 1024));
+  if (dtype == MASW_BF16)
+    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(blocks, a.B), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<float>, dim3(blocks, a.B), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? MASW_OK : MASW_ERR_LAUNCH;
+}
+
+}  // namespace masw

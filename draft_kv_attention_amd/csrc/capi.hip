@@ -1,0 +1,307 @@
+// capi.hip - the extern "C" entry points declared in include/masw.h: host-side
+// validation, the split-K plan, workspace carving and kernel dispatch.  Nothing here
+// touches device memory or synchronizes; every call only enqueues on `stream`.
+#include <algorithm>
+#include <cmath>
+
+#include "masw_internal.hpp"
+
+using namespace masw;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxSplits = 1024;
+constexpr long kTargetWorkGroups = 512;   // two per CU on 256 CUs
+constexpr long kMinKeysPerSplit = 128;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool group_supported(int g) { return g == 1 || g == 2 || g == 3 || g == 4 || g == 6 || g == 8; }
+
+int check_dims(const masw_dims* d, bool masw_memory) {
+  if (!d) return MASW_ERR_ARG;
+  if (d->dtype != MASW_F32 && d->dtype != MASW_BF16) return MASW_ERR_DTYPE;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return MASW_ERR_SHAPE;
+  if (d->n_q_heads % d->n_kv_heads) return MASW_ERR_SHAPE;
+  if (!group_supported(d->n_q_heads / d->n_kv_heads)) return MASW_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return MASW_ERR_SHAPE;
+  if (d->num_splits < 0 || d->num_splits > kMaxSplits) return MASW_ERR_ARG;
+  if (masw_memory) {
+    if (d->sink < 0 || d->window < 1 || d->interval < 1 || d->interval > d->window || d->max_slots < 0)
+      return MASW_ERR_ARG;
+  }
+  return MASW_OK;
+}
+
+// Splits per (sequence, KV head): enough work-groups to cover the chip, but at least
+// ~128 keys each.  The kernels re-derive the chunk from the actual key count.
+int choose_splits(const masw_dims* d, long max_keys) {
+  if (d->num_splits > 0) return d->num_splits;
+  const long units = long(d->batch) * d->n_kv_heads;
+  long s = (kTargetWorkGroups + units - 1) / units;
+  s = std::min(s, std::max(1L, (max_keys + kMinKeysPerSplit - 1) / kMinKeysPerSplit));
+  return int(std::max(1L, std::min(s, long(kMaxSplits))));
+}
+
+long masw_max_keys(const masw_dims* d) { return long(d->sink) + d->window + d->max_slots + 1; }
+
+struct WsPlan {
+  size_t flags, part_o, part_ml, total;
+};
+
+WsPlan plan_workspace(const masw_dims* d, int splits, int rows_per_seq) {
+  WsPlan p;
+  const size_t rows = size_t(d->batch) * rows_per_seq;
+  p.flags = 0;
+  p.part_o = align_up(size_t(d->batch) * sizeof(int32_t));
+  const size_t po = splits > 1 ? rows * splits * d->head_dim * sizeof(float) : 0;
+  p.part_ml = p.part_o + align_up(po);
+  const size_t pml = splits > 1 ? rows * splits * 2 * sizeof(float) : 0;
+  p.total = p.part_ml + align_up(pml);
+  return p;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need) return MASW_ERR_WORKSPACE;
+  if (need && (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign))) return MASW_ERR_WORKSPACE;
+  return MASW_OK;
+}
+
+float scale_log2(const masw_dims* d) {
+  const float s = d->scale > 0.f ? d->scale : 1.0f / std::sqrt(float(d->head_dim));
+  return s * 1.4426950408889634f;
+}
+
+MemGeom masw_geom(const masw_dims* d) {
+  return MemGeom{d->sink, d->window, d->interval, d->window + d->interval, d->max_slots};
+}
+
+// A full cache is a memory in which every one of its max_len tokens is a sink.
+MemGeom full_geom(int max_len) { return MemGeom{max_len, 1, 1, 2, 0}; }
+
+void fill_common(DecodeArgs& a, const masw_dims* d, int splits, void* ws, const WsPlan& p) {
+  a.B = d->batch;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.n_splits = splits;
+  a.scale_log2 = scale_log2(d);
+  char* base = static_cast<char*>(ws);
+  a.part_o = splits > 1 ? reinterpret_cast<float*>(base + p.part_o) : nullptr;
+  a.part_ml = splits > 1 ? reinterpret_cast<float*>(base + p.part_ml) : nullptr;
+}
+
+int check_layer(const masw_dims* d, const masw_layer* L) {
+  if (!L || !L->k_ring || !L->v_ring || !L->n_slots) return MASW_ERR_ARG;
+  if (d->sink > 0 && (!L->k_sink || !L->v_sink)) return MASW_ERR_ARG;
+  if (d->max_slots > 0 && (!L->k_slot || !L->v_slot)) return MASW_ERR_ARG;
+  return MASW_OK;
+}
+
+const void* or_else(const void* p, const void* q) { return p ? p : q; }
+
+}  // namespace
+
+extern "C" {
+
+MASW_API int masw_abi_version(void) { return MASW_ABI_VERSION; }
+
+MASW_API const char* masw_status_string(int status) {
+  switch (status) {
+    case MASW_OK: return "ok";
+    case MASW_ERR_ARG: return "invalid argument";
+    case MASW_ERR_DTYPE: return "unsupported dtype";
+    case MASW_ERR_SHAPE: return "unsupported shape";
+    case MASW_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MASW_ERR_LAUNCH: return "kernel launch failed";
+    case MASW_ERR_UNIMPLEMENTED: return "not implemented in this build";
+    default: return "unknown status";
+  }
+}
+
+MASW_API size_t masw_workspace_bytes(const masw_dims* d, int32_t op, int32_t max_keys, int32_t n_q) {
+  const bool masw_op = op == MASW_OP_DRAFT_ATTN || op == MASW_OP_MATERIALIZE;
+  if (check_dims(d, masw_op) != MASW_OK) return 0;
+  if (masw_op) {
+    const int splits = choose_splits(d, masw_max_keys(d));
+    return plan_workspace(d, splits, d->n_q_heads).total;
+  }
+  if (max_keys < 1) return 0;
+  if (op == MASW_OP_FULLKV_DECODE) return plan_workspace(d, choose_splits(d, max_keys), d->n_q_heads).total;
+  if (op == MASW_OP_FULLKV_VERIFY) {
+    if (n_q < 1) return 0;
+    return plan_workspace(d, choose_splits(d, max_keys), d->n_q_heads * n_q).total;
+  }
+  return 0;
+}
+
+MASW_API int masw_evict_append(const masw_dims* d, const masw_layer* L, const masw_seq* seq,
+                               const void* k_new, const void* v_new, int32_t n_new,
+                               hipStream_t stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if ((st = check_layer(d, L))) return st;
+  if (!seq || !seq->seq_len || !seq->err || n_new < 0) return MASW_ERR_ARG;
+  if (n_new == 0) return MASW_OK;
+  if (!k_new || !v_new) return MASW_ERR_ARG;
+  AppendArgs a{};
+  a.k_sink = L->k_sink ? L->k_sink : L->k_ring;
+  a.v_sink = L->v_sink ? L->v_sink : L->v_ring;
+  a.k_ring = L->k_ring;
+  a.v_ring = L->v_ring;
+  a.sink_cap = d->sink;
+  a.g = masw_geom(d);
+  a.seq_len = seq->seq_len;
+  a.err = seq->err;
+  a.n_slots = L->n_slots;
+  a.max_len = 0;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.B = d->batch;
+  a.Hkv = d->n_kv_heads;
+  a.D = d->head_dim;
+  a.n_new = n_new;
+  return launch_append(a, d->dtype, stream);
+}
+
+MASW_API int fullkv_append(const masw_dims* d, void* k, void* v, int32_t max_len, const int32_t* seq_len,
+                           int32_t* err, const void* k_new, const void* v_new, int32_t n_new,
+                           hipStream_t stream) {
+  int st = check_dims(d, false);
+  if (st) return st;
+  if (!k || !v || !seq_len || !err || max_len < 1 || n_new < 0) return MASW_ERR_ARG;
+  if (n_new == 0) return MASW_OK;
+  if (!k_new || !v_new) return MASW_ERR_ARG;
+  AppendArgs a{};
+  a.k_sink = k;
+  a.v_sink = v;
+  a.k_ring = k;
+  a.v_ring = v;
+  a.sink_cap = max_len;
+  a.g = full_geom(max_len);
+  a.seq_len = seq_len;
+  a.err = err;
+  a.n_slots = nullptr;
+  a.max_len = max_len;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.B = d->batch;
+  a.Hkv = d->n_kv_heads;
+  a.D = d->head_dim;
+  a.n_new = n_new;
+  return launch_append(a, d->dtype, stream);
+}
+
+MASW_API int masw_draft_attn(const masw_dims* d, const masw_layer* L, const masw_seq* seq, const void* q,
+                             void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if ((st = check_layer(d, L))) return st;
+  if (!seq || !seq->seq_len || !seq->err || !q || !out) return MASW_ERR_ARG;
+  const int splits = choose_splits(d, masw_max_keys(d));
+  const WsPlan p = plan_workspace(d, splits, d->n_q_heads);
+  if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
+  DecodeArgs a{};
+  a.k[0] = or_else(L->k_sink, L->k_ring); a.k[1] = L->k_ring; a.k[2] = or_else(L->k_slot, L->k_ring);
+  a.v[0] = or_else(L->v_sink, L->v_ring); a.v[1] = L->v_ring; a.v[2] = or_else(L->v_slot, L->v_ring);
+  a.cap[0] = d->sink; a.cap[1] = d->window + d->interval; a.cap[2] = d->max_slots;
+  a.g = masw_geom(d);
+  a.seq_len = seq->seq_len;
+  a.err = seq->err;
+  a.n_slots = L->n_slots;
+  a.q = q;
+  a.out = out;
+  fill_common(a, d, splits, ws, p);
+  return launch_decode(a, d->dtype, d->head_dim, stream);
+}
+
+MASW_API int fullkv_decode_attn(const masw_dims* d, const void* k, const void* v, int32_t max_len,
+                                const int32_t* seq_len, int32_t* err, const void* q, void* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(d, false);
+  if (st) return st;
+  if (!k || !v || !seq_len || !err || !q || !out || max_len < 1) return MASW_ERR_ARG;
+  const int splits = choose_splits(d, max_len);
+  const WsPlan p = plan_workspace(d, splits, d->n_q_heads);
+  if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
+  DecodeArgs a{};
+  for (int s = 0; s < 3; ++s) { a.k[s] = k; a.v[s] = v; }
+  a.cap[0] = max_len; a.cap[1] = 0; a.cap[2] = 0;
+  a.g = full_geom(max_len);
+  a.seq_len = seq_len;
+  a.err = err;
+  a.max_len = max_len;
+  a.q = q;
+  a.out = out;
+  fill_common(a, d, splits, ws, p);
+  return launch_decode(a, d->dtype, d->head_dim, stream);
+}
+
+MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, const masw_seq* seq,
+                                   int32_t hidden, const void* h, const void* w_k_g, const void* w_v_g,
+                                   const void* q_slot, void* o_slot, int32_t include_self, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if ((st = check_layer(d, L))) return st;
+  if (!seq || !seq->seq_len || !seq->err || !h || !w_k_g || !w_v_g || !q_slot || !o_slot || hidden < 1)
+    return MASW_ERR_ARG;
+  if (d->dtype == MASW_BF16 && hidden % 8) return MASW_ERR_SHAPE;
+  const int splits = choose_splits(d, masw_max_keys(d));
+  const WsPlan p = plan_workspace(d, splits, d->n_q_heads);
+  if ((st = check_ws(ws, ws_bytes, p.total))) return st;
+  int32_t* active = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.flags);
+
+  ProjectArgs pa{};
+  pa.h = h;
+  pa.w_k = w_k_g;
+  pa.w_v = w_v_g;
+  pa.k_slot = L->k_slot;
+  pa.v_slot = L->v_slot;
+  pa.seq_len = seq->seq_len;
+  pa.n_slots = L->n_slots;
+  pa.err = seq->err;
+  pa.active = active;
+  pa.g = masw_geom(d);
+  pa.B = d->batch;
+  pa.Hkv = d->n_kv_heads;
+  pa.D = d->head_dim;
+  pa.hidden = hidden;
+  if ((st = launch_project(pa, d->dtype, stream))) return st;
+
+  DecodeArgs a{};
+  a.k[0] = or_else(L->k_sink, L->k_ring); a.k[1] = L->k_ring; a.k[2] = or_else(L->k_slot, L->k_ring);
+  a.v[0] = or_else(L->v_sink, L->v_ring); a.v[1] = L->v_ring; a.v[2] = or_else(L->v_slot, L->v_ring);
+  a.cap[0] = d->sink; a.cap[1] = d->window + d->interval; a.cap[2] = d->max_slots;
+  a.g = masw_geom(d);
+  a.seq_len = seq->seq_len;
+  a.err = seq->err;
+  a.active = active;
+  a.n_slots_out = L->n_slots;
+  a.back = d->interval;
+  a.self_slot = include_self ? 1 : 0;
+  a.q = q_slot;
+  a.out = o_slot;
+  fill_common(a, d, splits, ws, p);
+  return launch_decode(a, d->dtype, d->head_dim, stream);
+}
+
+MASW_API int fullkv_verify_attn(const masw_dims* d, const void* k, const void* v, int32_t max_len,
+                                const int32_t* seq_len, int32_t* err, int32_t n_q, const void* q, void* out,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(d, false);
+  if (st) return st;
+  if (!k || !v || !seq_len || !err || !q || !out || max_len < 1 || n_q < 1 || n_q > 16) return MASW_ERR_ARG;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return MASW_ERR_UNIMPLEMENTED;
+}
+
+MASW_API int masw_debug_keylist(const masw_dims* d, const masw_seq* seq, int32_t back, int32_t* out,
+                                int32_t max_keys, hipStream_t stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if (!seq || !seq->seq_len || !out || max_keys < 1 || back < 0) return MASW_ERR_ARG;
+  return launch_debug_keylist(masw_geom(d), seq->seq_len, d->batch, back, out, max_keys, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// masw_device.hpp - device helpers shared by the libmasw kernels (gfx950, wave64).
+//
+// The one key resolver below is used by every attention kernel and by the debug dump,
+// so the segment bookkeeping the tests compare bit-exactly is the bookkeeping the
+// attention actually reads through.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/masw.h"
+
+namespace masw {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bf16 = upper half of an IEEE binary32)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round to nearest, ties to even: add 0x7fff plus the lowest kept bit, then truncate.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float to_f32(float x) { return x; }
+  __device__ static float from_f32(float x) { return x; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static float to_f32(uint16_t x) { return bf16_to_f32(x); }
+  __device__ static uint16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions
+// ---------------------------------------------------------------------------
+// Sum over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1): every lane gets the total.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, false));
+  return v;
+}
+
+__device__ __forceinline__ float xor_lanes(float v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+// Combine across the four 16-lane rows of a wave.
+__device__ __forceinline__ float rows4_max(float v) {
+  v = fmaxf(v, xor_lanes(v, 16));
+  return fmaxf(v, xor_lanes(v, 32));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  v += xor_lanes(v, 16);
+  return v + xor_lanes(v, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Memory geometry and the key resolver (Technical Review §3.1, Eq. 4)
+// ---------------------------------------------------------------------------
+struct MemGeom {
+  int S;          // sink count (a full cache is a memory whose every token is a sink)
+  int W;          // local window
+  int r;          // slot interval
+  int C;          // ring rows, W + r
+  int max_slots;  // slot rows per (sequence, KV head)
+};
+
+// Counts of keylist(t): sinks, local window, slots; lo = first local position,
+// ring0 = ring row of position lo.
+struct KeySpan {
+  int ns, nl, nslot, lo, ring0;
+  __device__ int total() const { return ns + nl + nslot; }
+};
+
+__device__ __forceinline__ KeySpan key_span(int t, const MemGeom& g) {
+  KeySpan k;
+  k.ns = min(g.S, t);
+  k.nl = min(max(t - g.S, 0), g.W);
+  k.lo = t - k.nl + 1;
+  int d = t - g.S - g.W;
+  k.nslot = d > 0 ? d / g.r : 0;
+  k.ring0 = k.nl > 0 ? (k.lo - g.S - 1) % g.C : 0;
+  return k;
+}
+
+struct KeyRef {
+  int seg;  // 0 sink, 1 ring, 2 slot
+  int row;  // row inside that segment's [rows][D] block
+  int id;   // raw position (sink / ring) or slot index m
+};
+
+// Logical key j (0-based, order sink ++ local ++ slots) -> physical row.
+__device__ __forceinline__ KeyRef resolve_key(int j, const KeySpan& k, const MemGeom& g) {
+  KeyRef r;
+  if (j < k.ns) {
+    r.seg = 0; r.row = j; r.id = j + 1;
+  } else if (j < k.ns + k.nl) {
+    int o = j - k.ns;
+    int c = k.ring0 + o;
+    if (c >= g.C) c -= g.C;
+    r.seg = 1; r.row = c; r.id = k.lo + o;
+  } else {
+    int m = j - k.ns - k.nl;
+    r.seg = 2; r.row = m; r.id = m + 1;
+  }
+  return r;
+}
+
+}  // namespace masw

@@ -1,0 +1,75 @@
+// masw_internal.hpp - argument blocks and launchers between the C ABI (capi.hip) and
+// the kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "masw_device.hpp"
+
+namespace masw {
+
+// Keys per wave iteration of the decode kernel: 4 rows of 16 lanes x 8 rows per lane.
+constexpr int kDecodeTileKeys = 32;
+constexpr int kDecodeThreads = 256;
+
+// Split-K decode attention over one memory (three segments; a full cache is the sink
+// segment alone).  One work-group per (split, KV head, sequence).
+struct DecodeArgs {
+  const void* k[3];   // segment bases: sink, ring, slot
+  const void* v[3];
+  int cap[3];         // rows per (sequence, KV head) in each segment
+  MemGeom g;
+  const int32_t* seq_len;
+  int32_t* err;
+  const int32_t* n_slots;   // MASW decode: checked against n(t); null for a full cache
+  const int32_t* active;    // slot-query mode: per-sequence slot index m (0 = skip)
+  int32_t* n_slots_out;     // slot-query mode: set to m once the query is written
+  int back;                 // keys of keylist(t - back)
+  int self_slot;            // slot-query mode: also attend to the new slot itself
+  int max_len;              // full cache: t must not exceed it (0: no bound)
+  const void* q;            // [B][Hq][D]
+  void* out;                // [B][Hq][D]
+  float* part_o;            // [B][Hq][splits][D]
+  float* part_ml;           // [B][Hq][splits][2]  (running max in log2 units, sum)
+  int B, Hq, Hkv, n_splits;
+  float scale_log2;         // softmax scale times log2(e)
+};
+
+int launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t s);
+int launch_debug_keylist(const MemGeom& g, const int32_t* seq_len, int B, int back,
+                         int32_t* out, int max_keys, hipStream_t s);
+
+// Append raw tokens into a memory (sink + ring; a full cache is all sink).
+struct AppendArgs {
+  void* k_sink; void* v_sink;
+  void* k_ring; void* v_ring;
+  int sink_cap;             // rows per (sequence, KV head) of the sink block
+  MemGeom g;
+  const int32_t* seq_len;
+  int32_t* err;
+  const int32_t* n_slots;   // null for a full cache
+  int max_len;              // full cache bound (0: none)
+  const void* k_new; const void* v_new;   // [B][n_new][Hkv][D]
+  int B, Hkv, D, n_new;
+};
+
+int launch_append(const AppendArgs& a, int dtype, hipStream_t s);
+
+// Mirrored projection of the slot hidden state into slot row m-1, plus the
+// per-sequence boundary decision written to `active`.
+struct ProjectArgs {
+  const void* h;            // [B][hidden]
+  const void* w_k; const void* w_v;   // [hidden][Hkv*D]
+  void* k_slot; void* v_slot;         // [B][Hkv][max_slots][D]
+  const int32_t* seq_len;
+  const int32_t* n_slots;
+  int32_t* err;
+  int32_t* active;          // [B] workspace
+  MemGeom g;
+  int B, Hkv, D, hidden;
+};
+
+int launch_project(const ProjectArgs& a, int dtype, hipStream_t s);
+
+}  // namespace masw

@@ -1,0 +1,214 @@
+/*
+ * masw.h - C ABI of libmasw.so: the hot path of Memory-Augmented Sliding-Window (MASW)
+ * drafting on AMD MI355X (gfx950).
+ *
+ * Pages cited (title; section / equation / algorithm step on that page):
+ *   [TR] "Strong Drafts Need Compact Memories: A Technical Review of Memory-Augmented
+ *        Sliding-Window (MASW) Drafting for Long-Context Speculative Decoding".
+ *
+ * Notation follows [TR]: S sink tokens, W local-window width, r slot interval,
+ * t = number of raw tokens in a sequence's cache INCLUDING the token(s) being appended
+ * or queried this step (Eq. 2 attends over K_{<=t}); positions are 1-based; g_m is the
+ * m-th memory slot.  The draft memory at step t is ([TR] §3.1, Eq. 4)
+ *     keylist(t) = sinks 1..min(S,t)  ++  local max(S+1, t-W+1)..t  ++  slots 1..n(t)
+ * with n(t) = floor(max(0, t-S-W) / r).  Slot g_m compresses raw positions
+ * S+(m-1)r+1 .. S+mr and is materialized at step t_m = S + W + m*r ([TR] §3.2,
+ * Algorithm 1), after raw token t_m is appended and before the decode query at t_m.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Ownership: every pointer argument is DEVICE memory owned by the caller.  The
+ *    library allocates nothing, keeps no global state and is thread-safe.
+ *  - Streams: every call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *    legacy default stream).  No call synchronizes or reads device memory on the host,
+ *    so a sequence of calls can be captured into a HIP graph.
+ *  - Return value: MASW_OK or a negative MASW_ERR_* for errors found on the host before
+ *    anything is enqueued (or MASW_ERR_LAUNCH if a launch fails).  Nothing is enqueued
+ *    when a host error is returned.
+ *  - Device errors: violations only the device can see (they depend on seq_len and
+ *    n_slots) are OR-ed into the caller's sticky int32 error word `*err` as
+ *    MASW_DEV_* bits, and the offending sequence's writes are suppressed (its output,
+ *    cache rows or slot stay untouched).  The caller clears *err when it wants.
+ *  - Layouts are row-major with the last index contiguous.  bf16 tensors hold IEEE
+ *    bfloat16 bit patterns; results are rounded to nearest-even.  Accumulation is fp32.
+ *  - Workspace: ops that split the key range (flash-decoding split-K) need a scratch
+ *    buffer of at least masw_workspace_bytes(...) bytes, 256-byte aligned, that no other
+ *    call uses concurrently.  Its contents need no initialization.
+ */
+#ifndef MASW_H_
+#define MASW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MASW_API __attribute__((visibility("default")))
+#define MASW_ABI_VERSION 1
+
+/* ---- host status codes ------------------------------------------------------- */
+enum {
+  MASW_OK = 0,
+  MASW_ERR_ARG = -1,           /* a null pointer, a negative size, r outside 1..W ... */
+  MASW_ERR_DTYPE = -2,         /* dtype not MASW_F32 / MASW_BF16                     */
+  MASW_ERR_SHAPE = -3,         /* Hq % Hkv != 0, head_dim not 64/128, group > 8 ...   */
+  MASW_ERR_WORKSPACE = -4,     /* workspace missing, too small or misaligned          */
+  MASW_ERR_LAUNCH = -5,        /* hipGetLastError() reported a launch failure         */
+  MASW_ERR_UNIMPLEMENTED = -6  /* a valid request this build does not support         */
+};
+
+/* ---- device error bits (OR-ed into *err) -------------------------------------- */
+enum {
+  MASW_DEV_PENDING_SLOT = 1,  /* an append would overwrite a raw token whose block has
+                                 no slot yet; that token's write was suppressed          */
+  MASW_DEV_SLOT_CAPACITY = 2, /* a step needs more than max_slots slots                  */
+  MASW_DEV_SEQ_RANGE = 4,     /* seq_len out of range (t < 1 for a query, t < n_new for
+                                 an append, t > max_len for a full cache, t < n_q ...)   */
+  MASW_DEV_SLOT_MISSING = 8   /* a query needs slot n(t) (or a boundary needs slot m-1)
+                                 but n_slots says it was never materialized              */
+};
+
+typedef enum { MASW_F32 = 0, MASW_BF16 = 1 } masw_dtype;
+
+/* Geometry and memory parameters.  S, W, r and max_slots are ignored by the
+ * full-KV entry points. */
+typedef struct {
+  int32_t batch;       /* B >= 1 sequences                                         */
+  int32_t n_q_heads;   /* Hq; query head h reads KV head h / (Hq/Hkv) (grouped)     */
+  int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0 and Hq/Hkv in {1,2,3,4,6,8}           */
+  int32_t head_dim;    /* D in {64, 128}                                           */
+  int32_t sink;        /* S >= 0                                                   */
+  int32_t window;      /* W >= 1                                                   */
+  int32_t interval;    /* r, 1 <= r <= W; the local ring holds C = W + r rows       */
+  int32_t max_slots;   /* slot rows allocated per (sequence, KV head), >= 0         */
+  int32_t dtype;       /* masw_dtype of every K/V/q/out/h/w tensor                 */
+  float scale;         /* softmax scale; <= 0 selects 1/sqrt(D) ([TR] §2.3 Eq. 2)  */
+  int32_t num_splits;  /* split-K plan: 0 = library heuristic, else splits per
+                          (sequence, KV head) in 1..1024.  Two calls over the same
+                          keys with the same value give bitwise equal results.     */
+} masw_dims;
+
+/* One layer's compact draft memory ([TR] §3.1 Eq. 4).  Layouts:
+ *   k_sink, v_sink [B][Hkv][S][D]      sink cell i-1 holds position i (i <= S)
+ *   k_ring, v_ring [B][Hkv][W+r][D]    ring cell (i-S-1) mod (W+r) holds position i > S
+ *   k_slot, v_slot [B][Hkv][max_slots][D]  slot row m-1 holds g_m
+ *   n_slots [B]                        slots materialized so far in THIS layer       */
+typedef struct {
+  void* k_sink;
+  void* v_sink;
+  void* k_ring;
+  void* v_ring;
+  void* k_slot;
+  void* v_slot;
+  int32_t* n_slots;
+} masw_layer;
+
+/* Per-sequence step state shared by all layers of a step. */
+typedef struct {
+  const int32_t* seq_len;  /* [B] t of each sequence (advanced by the caller once per
+                              step, before that step's appends)                     */
+  int32_t* err;            /* [1] sticky MASW_DEV_* bits                             */
+} masw_seq;
+
+/* Operation ids for masw_workspace_bytes. */
+enum {
+  MASW_OP_DRAFT_ATTN = 0,
+  MASW_OP_MATERIALIZE = 1,
+  MASW_OP_FULLKV_DECODE = 2,
+  MASW_OP_FULLKV_VERIFY = 3
+};
+
+/* Raw append with implicit eviction ([TR] §3.2 Algorithm 1 step 5; Eq. 4 local bullet).
+ * k_new, v_new [B][n_new][Hkv][D] hold positions t-n_new+1 .. t (t = seq_len[b]).
+ * Position i <= S goes to sink cell i-1; i > S to ring cell (i-S-1) mod (W+r), which
+ * evicts the token i-(W+r) that occupied it.  That eviction is legal only if the
+ * evicted token is a never-written cell or its block's slot already exists
+ * (n_slots[b] >= ceil((i-(W+r)-S)/r)); otherwise the token is not written and
+ * MASW_DEV_PENDING_SLOT is set.  t < n_new sets MASW_DEV_SEQ_RANGE and writes nothing.
+ * n_new == 0 is a no-op. */
+MASW_API int masw_evict_append(const masw_dims* dims, const masw_layer* layer,
+                               const masw_seq* seq, const void* k_new, const void* v_new,
+                               int32_t n_new, hipStream_t stream);
+
+/* Slot materialization at a compression boundary ([TR] §3.2 Algorithm 1 steps 2-4).
+ * For each sequence, the call acts only if t = seq_len[b] is the boundary of slot
+ * m = (t-S-W)/r >= 1 and n_slots[b] == m-1; otherwise it leaves that sequence alone
+ * (n_slots[b] == m: already done, silent; n_slots[b] < m-1: MASW_DEV_SLOT_MISSING;
+ * m > max_slots: MASW_DEV_SLOT_CAPACITY).  For an acting sequence:
+ *   1. mirrored projection (Algorithm 1 step 3): K_g = H W_K,g, V_g = H W_V,g with
+ *      h [B][hidden], w_k_g, w_v_g [hidden][Hkv*D] (KV head k = columns k*D..k*D+D-1),
+ *      stored (rounded to the cache dtype) into slot row m-1;
+ *   2. the slot query (Algorithm 1 step 2, structured mask): q_slot [B][Hq][D] attends
+ *      over keylist(t - r) = sinks ++ the W-window whose oldest r tokens are the block
+ *      g_m compresses ++ slots 1..m-1 (plus g_m itself if include_self != 0), and the
+ *      result is written to o_slot [B][Hq][D];
+ *   3. n_slots[b] = m (Algorithm 1 step 4).
+ * q_slot is an input because only K/V projections are mirrored.  hidden >= 1. */
+MASW_API int masw_materialize_slot(const masw_dims* dims, const masw_layer* layer,
+                                   const masw_seq* seq, int32_t hidden, const void* h,
+                                   const void* w_k_g, const void* w_v_g, const void* q_slot,
+                                   void* o_slot, int32_t include_self, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/* MASW draft decode attention ([TR] §2.3 Eq. 2 over §3.1 Eq. 4; §3.3 Algorithm 2 step 4).
+ * q, out [B][Hq][D]: out[b][h] = softmax(scale * q K^T) V over keylist(seq_len[b]) of
+ * KV head h / (Hq/Hkv).  Needs 1 <= t (else MASW_DEV_SEQ_RANGE), n(t) <= max_slots
+ * (else MASW_DEV_SLOT_CAPACITY) and n_slots[b] >= n(t) (else MASW_DEV_SLOT_MISSING);
+ * a sequence failing a check keeps its old output. */
+MASW_API int masw_draft_attn(const masw_dims* dims, const masw_layer* layer,
+                             const masw_seq* seq, const void* q, void* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Full-KV draft decode attention, the baseline ([TR] §2.3 Eq. 2 over K_{<=t}).
+ * k, v [B][Hkv][max_len][D] (row i-1 holds position i); q, out [B][Hq][D]; keys 1..t.
+ * Runs the same kernel as masw_draft_attn with a one-segment memory, so for
+ * t <= S + W and equal num_splits both give bitwise equal outputs.
+ * t < 1 or t > max_len: MASW_DEV_SEQ_RANGE, output untouched. */
+MASW_API int fullkv_decode_attn(const masw_dims* dims, const void* k, const void* v,
+                                int32_t max_len, const int32_t* seq_len, int32_t* err,
+                                const void* q, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Full-KV append: writes positions t-n_new+1..t to rows t-n_new..t-1 of
+ * k, v [B][Hkv][max_len][D] from k_new, v_new [B][n_new][Hkv][D].  t < n_new or
+ * t > max_len: MASW_DEV_SEQ_RANGE, nothing written. */
+MASW_API int fullkv_append(const masw_dims* dims, void* k, void* v, int32_t max_len,
+                           const int32_t* seq_len, int32_t* err, const void* k_new,
+                           const void* v_new, int32_t n_new, hipStream_t stream);
+
+/* Verifier attention over the full cache ([TR] §3.3 Algorithm 2 step 5): n_q candidate
+ * positions checked in one parallel pass.  q, out [B][n_q][Hq][D]; query j sits at
+ * position t-n_q+1+j (t = seq_len[b], the candidates already appended) and attends to
+ * keys 1 .. t-n_q+1+j (causal among the candidates).  1 <= n_q <= 16.
+ * t < n_q or t > max_len: MASW_DEV_SEQ_RANGE, output untouched. */
+MASW_API int fullkv_verify_attn(const masw_dims* dims, const void* k, const void* v,
+                                int32_t max_len, const int32_t* seq_len, int32_t* err,
+                                int32_t n_q, const void* q, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes an op needs.  max_keys: for the full-KV ops, max_len; ignored by the
+ * MASW ops (their bound is S + W + max_slots + 1).  n_q: verifier candidates (others
+ * ignore it).  Returns 0 for invalid dims. */
+MASW_API size_t masw_workspace_bytes(const masw_dims* dims, int32_t op, int32_t max_keys,
+                                     int32_t n_q);
+
+/* Human-readable text of a MASW_OK / MASW_ERR_* code (static storage). */
+MASW_API const char* masw_status_string(int status);
+
+/* MASW_ABI_VERSION of the built library. */
+MASW_API int masw_abi_version(void);
+
+/* Test hook: the device key resolver used by every attention kernel, dumped.  For
+ * each sequence b and logical key j of keylist(seq_len[b] - back) it writes
+ * out[b][j] = {segment (0 sink, 1 ring, 2 slot), row, id (position or slot index)};
+ * unused entries up to max_keys are {-1,-1,-1}.  out [B][max_keys][3] int32. */
+MASW_API int masw_debug_keylist(const masw_dims* dims, const masw_seq* seq, int32_t back,
+                                int32_t* out, int32_t max_keys, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MASW_H_ */

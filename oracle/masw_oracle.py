@@ -209,10 +209,14 @@ class DraftMemory:
 
     # -- writes ------------------------------------------------------------
     def append(self, k_new: np.ndarray, v_new: np.ndarray) -> None:
-        """Append raw tokens t+1..t+n (k_new, v_new [n][Hkv][D]); eviction is implicit."""
+        """Append raw tokens t+1..t+n (k_new, v_new [n][Hkv][D]); eviction is implicit.
+
+        Values are kept as passed (an fp32 array holds bf16/fp32 inputs exactly) and
+        widened to fp64 when gathered.
+        """
         for j in range(k_new.shape[0]):
             self.t += 1
-            self.raw[self.t] = (np.asarray(k_new[j], np.float64), np.asarray(v_new[j], np.float64))
+            self.raw[self.t] = (np.asarray(k_new[j]), np.asarray(v_new[j]))
 
     def pending_boundary(self) -> int:
         """m if the current step materializes g_m and it does not exist yet, else 0."""
@@ -242,7 +246,7 @@ class DraftMemory:
             k, v = self.raw[idx] if kind == "raw" else self.slots[idx]
             ks.append(k)
             vs.append(v)
-        return np.stack(ks, axis=1), np.stack(vs, axis=1)
+        return np.stack(ks, axis=1).astype(np.float64), np.stack(vs, axis=1).astype(np.float64)
 
     def decode(self, q: np.ndarray, scale: float) -> np.ndarray:
         """Draft decode attention at the current step over M_t ([TR] §3.3 Algorithm 2 step 4)."""

@@ -1,0 +1,95 @@
+"""Host-side checks of the C ABI that need no GPU: every symbol include/masw.h declares
+is exported by libmasw.so, the ABI version matches, and invalid arguments are rejected
+on the host before anything would be enqueued (these calls never reach a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_kv_attention_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "masw.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.LIB_PATH):
+        from draft_kv_attention_amd import build
+        build.build()
+    return M.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"MASW_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_five_entry_points():
+    names = set(declared_symbols())
+    for n in ("masw_draft_attn", "masw_materialize_slot", "masw_evict_append",
+              "fullkv_decode_attn", "fullkv_verify_attn"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.masw_abi_version() == int(re.search(r"MASW_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+
+
+def _dims(**kw):
+    base = dict(batch=2, n_q_heads=24, n_kv_heads=8, head_dim=128, sink=4, window=2048, interval=64,
+                max_slots=100, dtype=M.BF16, scale=0.0, num_splits=0)
+    base.update(kw)
+    return M._Dims(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(interval=0), -1), (dict(interval=2049), -1), (dict(sink=-1), -1), (dict(max_slots=-1), -1),
+    (dict(n_q_heads=20), -3), (dict(head_dim=96), -3), (dict(n_q_heads=40, n_kv_heads=8), -3),
+    (dict(dtype=7), -2), (dict(num_splits=5000), -1), (dict(batch=0), -3)])
+def test_invalid_dims_rejected_on_host(lib, kw, status):
+    d = _dims(**kw)
+    assert lib.masw_draft_attn(ctypes.byref(d), None, None, None, None, None, 0, None) == status
+    assert lib.masw_workspace_bytes(ctypes.byref(d), M.OP_DRAFT_ATTN, 0, 0) == 0
+
+
+def test_null_arguments_rejected_on_host(lib):
+    d = _dims()
+    assert lib.masw_draft_attn(None, None, None, None, None, None, 0, None) == -1
+    assert lib.masw_draft_attn(ctypes.byref(d), None, None, None, None, None, 0, None) == -1
+    layer = M._Layer(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    seq = M._Seq(1 << 20, 1 << 20)
+    # workspace missing while the plan splits the key range
+    assert lib.masw_draft_attn(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq),
+                               1 << 20, 1 << 20, None, 0, None) == -4
+    # misaligned workspace
+    need = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_DRAFT_ATTN, 0, 0)
+    assert lib.masw_draft_attn(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq),
+                               1 << 20, 1 << 20, (1 << 20) + 8, need, None) == -4
+    assert lib.masw_evict_append(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq),
+                                 None, None, -1, None) == -1
+    # n_new == 0 is a no-op that enqueues nothing
+    assert lib.masw_evict_append(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq),
+                                 None, None, 0, None) == 0
+    assert lib.fullkv_verify_attn(ctypes.byref(d), 1, 1, 10, 1, 1, 0, 1, 1, None, 0, None) == -1
+    assert lib.masw_materialize_slot(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq), 3071,
+                                     1, 1, 1, 1, 1, 0, 1 << 20, 1 << 30, None) == -3
+
+
+def test_workspace_sizes(lib):
+    d = _dims(batch=8)
+    a = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_DRAFT_ATTN, 0, 0)
+    b = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_MATERIALIZE, 0, 0)
+    f = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_FULLKV_DECODE, 32768, 0)
+    v = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_FULLKV_VERIFY, 32774, 6)
+    assert a > 0 and b == a and f > 0 and v > 0
+    assert lib.masw_workspace_bytes(ctypes.byref(d), M.OP_FULLKV_DECODE, 0, 0) == 0
+    assert all(x % 256 == 0 for x in (a, b, f, v))
+
+
+def test_status_strings(lib):
+    for st in range(-6, 1):
+        assert M.status_string(st) not in ("", "unknown status")

@@ -121,22 +121,23 @@ class Stack:
 
     # -- one step ----------------------------------------------------------
     def masw_step(self, boundary):
+        """One decode position: per layer, the slot materialization when the step is a
+        boundary (it reads only older tokens, so it may precede the append), then the
+        fused raw append + draft attention."""
         self.seq.seq_len.add_(1)
         for l in range(self.L):
             lay = self.layers[l]
-            M.masw_evict_append(self.d, lay, self.seq, self.k_new[l], self.v_new[l])
             if boundary:
                 M.masw_materialize_slot(self.d, lay, self.seq, self.h[l], self.wk[l], self.wv[l],
                                         self.qg[l], self.og[l], self.ws)
-            M.masw_draft_attn(self.d, lay, self.seq, self.q[l], self.out[l], self.ws)
+            M.masw_decode_step(self.d, lay, self.seq, self.k_new[l], self.v_new[l], self.q[l],
+                               self.out[l], self.ws)
 
     def full_step(self):
         self.seq_full.add_(1)
         for l in range(self.L):
-            M.fullkv_append(self.fd, self.kf[l], self.vf[l], self.seq_full, self.err_full,
-                            self.k_new[l], self.v_new[l])
-            M.fullkv_decode_attn(self.fd, self.kf[l], self.vf[l], self.seq_full, self.err_full,
-                                 self.q[l], self.out[l], self.ws_full)
+            M.fullkv_decode_step(self.fd, self.kf[l], self.vf[l], self.seq_full, self.err_full,
+                                 self.k_new[l], self.v_new[l], self.q[l], self.out[l], self.ws_full)
 
     def capture(self):
         """Capture the three step variants; each capture advances nothing (state is reset)."""
@@ -207,33 +208,126 @@ def time_steps(stack, which, t_start, warmup, steps):
     return ms, avg_bytes
 
 
-def kernel_roofline(stack, t, reps=4):
-    """Average duration of one masw_draft_attn call, from events around each call.
+def graph_per_call_us(fn, calls, replays=5):
+    """Average duration of one call inside a captured graph of `calls` back-to-back calls."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(calls):
+            fn(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(calls):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * calls)
 
-    A spin kernel first gives the host a head start, so every call is already queued
-    when the GPU reaches it and each event pair brackets only the call's own kernels.
+
+def kernel_roofline(stack, t, reps=4):
+    """The dominant kernel of the MASW step: the fused append + draft attention launch.
+
+    Average launch duration from HIP events around graph replays of 28 layers x reps
+    back-to-back launches at prefix t (distinct per-layer buffers, 2.3 GB per pass, so
+    nothing is served from the 256 MB last-level cache).  Algorithmic bytes per launch:
+    the working set's K and V read once, q read, out written, the new token read from
+    the caller and written into the ring.
     """
     stack.set_position(t)
-    evs = []
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.4e9 * 0.05))
-    for _ in range(reps):
-        for l in range(stack.L):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            M.masw_draft_attn(stack.d, stack.layers[l], stack.seq, stack.q[l], stack.out[l], stack.ws)
-            b.record()
-            evs.append((a, b))
-    torch.cuda.synchronize()
-    durs = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)   # us
-    avg_us = float(np.mean(durs))
-    nbytes = stack.attn_bytes(keys_at(t, stack.S, stack.W, stack.r))
-    achieved = nbytes / (avg_us * 1e-6) / 1e9
+    L = stack.L
+    us = graph_per_call_us(lambda i: M.masw_decode_step(stack.d, stack.layers[i % L], stack.seq,
+                                                        stack.k_new[i % L], stack.v_new[i % L],
+                                                        stack.q[i % L], stack.out[i % L], stack.ws),
+                           L * reps)
+    sh = stack.shape
+    nbytes = stack.attn_bytes(keys_at(t, stack.S, stack.W, stack.r)) + 2 * sh.batch * stack.kv_row_bytes()
+    achieved = nbytes / (us * 1e-6) / 1e9
     return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                kernel="masw_draft_attn", avg_us=round(avg_us, 2),
-                median_us=round(float(np.median(durs)), 2), bytes_per_launch=int(nbytes),
-                prefix=t, launches=len(durs))
+                kernel="decode_kernel<bf16,128,3> (masw_decode_step)", avg_us=round(us, 2),
+                bytes_per_launch=int(nbytes), prefix=t, launches_timed=L * reps * 5)
+
+
+def verify_leg(dev, prefix=32768, n_q=6, batch=4):
+    """Verifier attention, one GPU's share of an 8B / 70B layer (8 KV heads)."""
+    out = []
+    t = prefix + n_q
+    for Hq in (32, 64):
+        vd = M.Dims(batch=batch, n_q_heads=Hq, n_kv_heads=8, head_dim=128, dtype=torch.bfloat16)
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        kv = [torch.randn(batch, 8, t + 8, 128, device=dev, dtype=torch.bfloat16, generator=g) for _ in range(2)]
+        vv = [torch.randn(batch, 8, t + 8, 128, device=dev, dtype=torch.bfloat16, generator=g) for _ in range(2)]
+        qv = torch.randn(batch, n_q, Hq, 128, device=dev, dtype=torch.bfloat16, generator=g)
+        ov = torch.empty_like(qv)
+        sv = torch.full((batch,), t, dtype=torch.int32, device=dev)
+        ev = torch.zeros(1, dtype=torch.int32, device=dev)
+        wsv = M.workspace(vd, M.OP_FULLKV_VERIFY, max_keys=t + 8, n_q=n_q, device=dev)
+        us = graph_per_call_us(lambda i: M.fullkv_verify_attn(vd, kv[i % 2], vv[i % 2], sv, ev, qv, ov, wsv), 8)
+        nbytes = batch * (t * 8 * 128 * 2 * 2 + 2 * n_q * Hq * 128 * 2)
+        flops = 4.0 * batch * n_q * Hq * 128 * t
+        out.append(dict(shape=f"{Hq}q/8kv heads, prefix {prefix}+{n_q}, batch {batch}", us_per_layer=round(us, 2),
+                        gbs=round(nbytes / us / 1e3, 1), pct_peak=round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1),
+                        tflops=round(flops / us / 1e6, 1), err_bits=int(ev.item())))
+        del kv, vv
+        torch.cuda.empty_cache()
+    return out
+
+
+def materialize_leg(stack, t_boundary, replays=5):
+    """One slot boundary across the 28 layers (projection + structured-mask slot query).
+
+    Each replay first resets every layer's n_slots to m-1 (so the boundary is pending
+    again); a graph holding only those resets is timed separately and subtracted.
+    """
+    L = stack.L
+    stack.set_position(t_boundary)
+    m = (t_boundary - stack.S - stack.W) // stack.r
+
+    def resets():
+        for lay in stack.layers:
+            lay.n_slots.fill_(m - 1)
+
+    def boundary():
+        resets()
+        for i in range(L):
+            M.masw_materialize_slot(stack.d, stack.layers[i], stack.seq, stack.h[i], stack.wk[i], stack.wv[i],
+                                    stack.qg[i], stack.og[i], stack.ws)
+
+    times = {}
+    for name, fn in (("resets", resets), ("boundary", boundary)):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) * 1e3 / replays
+    per_layer = (times["boundary"] - times["resets"]) / L
+    sh = stack.shape
+    keys = stack.S + stack.W + m - 1
+    nbytes = (2 * sh.hidden * sh.n_kv_heads * sh.head_dim * 2 + sh.batch * sh.hidden * 2
+              + stack.attn_bytes(keys) + sh.batch * stack.kv_row_bytes())
+    return dict(slot_index=m, us_per_layer=round(per_layer, 2), bytes_per_layer=int(nbytes),
+                gbs=round(nbytes / per_layer / 1e3, 1), per_decode_step_us=round(per_layer * L / stack.r, 2),
+                slots_after=int(stack.layers[0].n_slots[0].item()))
 
 
 def cpu_baseline(budget_s=15.0):
@@ -320,6 +414,12 @@ def main():
     roof = kernel_roofline(stack, T_HEAD)
     print(f"[bench] roofline {roof}", file=sys.stderr, flush=True)
     err_bits = int(stack.seq.err.item()) | int(stack.err_full.item())
+    mat = materialize_leg(stack, 2052 + 480 * 64)
+    print(f"[bench] materialization {mat}", file=sys.stderr, flush=True)
+    del stack
+    torch.cuda.empty_cache()
+    ver = verify_leg(dev)
+    print(f"[bench] verifier {ver}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -339,6 +439,7 @@ def main():
         "hbm_gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(value * sh.batch, 1),
         "fullkv_at_prefix": full_head, "sweep": sweep, "device_err_bits": err_bits,
+        "materialization": mat, "verifier": ver,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

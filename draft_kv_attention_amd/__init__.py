@@ -72,6 +72,10 @@ _SIGS = {
                                           ctypes.c_size_t, _P]),
     "fullkv_append": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
                                      ctypes.c_int32, _P]),
+    "masw_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
+    "fullkv_decode_step": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
+                                          ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "fullkv_verify_attn": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32,
                                           _P, _P, _P, ctypes.c_size_t, _P]),
     "masw_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
@@ -181,10 +185,11 @@ def workspace_bytes(d: Dims, op: int, max_keys: int = 0, n_q: int = 0) -> int:
 
 
 def workspace(d: Dims, op: int, max_keys: int = 0, n_q: int = 0, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace (the split tickets must start at zero; calls keep them so)."""
     n = workspace_bytes(d, op, max_keys, n_q)
     if n == 0:
         raise MaswError("masw_workspace_bytes", -1)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------------------
@@ -279,6 +284,24 @@ def masw_draft_attn(d: Dims, layer: Layer, seq: Seq, q: torch.Tensor, out: torch
         wp, wb, _stream(stream)))
 
 
+def masw_decode_step(d: Dims, layer: Layer, seq: Seq, k_new: torch.Tensor, v_new: torch.Tensor,
+                     q: torch.Tensor, out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """Fused append of positions t-n+1..t ([B][n][Hkv][D]) and draft attention."""
+    _check_layer(d, layer)
+    _check_seq(d, seq)
+    n = k_new.shape[1]
+    for nm, t in (("k_new", k_new), ("v_new", v_new)):
+        _check(t, nm, (d.batch, n, d.n_kv_heads, d.head_dim), d.dtype)
+    for nm, t in (("q", q), ("out", out)):
+        _check(t, nm, (d.batch, d.n_q_heads, d.head_dim), d.dtype)
+    wp, wb = _ws(workspace)
+    dc, lc, sc = d.c(), layer.c(), seq.c()
+    _ok("masw_decode_step", lib().masw_decode_step(
+        ctypes.byref(dc), ctypes.byref(lc), ctypes.byref(sc), k_new.data_ptr(), v_new.data_ptr(), n,
+        q.data_ptr(), out.data_ptr(), wp, wb, _stream(stream)))
+
+
 def _check_full(d: Dims, k, v, seq_len, err):
     max_len = k.shape[2]
     for nm, t in (("k", k), ("v", v)):
@@ -313,6 +336,23 @@ def fullkv_append(d: Dims, k: torch.Tensor, v: torch.Tensor, seq_len: torch.Tens
     _ok("fullkv_append", lib().fullkv_append(
         ctypes.byref(dc), k.data_ptr(), v.data_ptr(), max_len, seq_len.data_ptr(), err.data_ptr(),
         k_new.data_ptr(), v_new.data_ptr(), n, _stream(stream)))
+
+
+def fullkv_decode_step(d: Dims, k: torch.Tensor, v: torch.Tensor, seq_len: torch.Tensor,
+                       err: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                       out: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Fused full-cache append of positions t-n+1..t and decode attention."""
+    max_len = _check_full(d, k, v, seq_len, err)
+    n = k_new.shape[1]
+    for nm, t in (("k_new", k_new), ("v_new", v_new)):
+        _check(t, nm, (d.batch, n, d.n_kv_heads, d.head_dim), d.dtype)
+    for nm, t in (("q", q), ("out", out)):
+        _check(t, nm, (d.batch, d.n_q_heads, d.head_dim), d.dtype)
+    wp, wb = _ws(workspace)
+    dc = d.c()
+    _ok("fullkv_decode_step", lib().fullkv_decode_step(
+        ctypes.byref(dc), k.data_ptr(), v.data_ptr(), max_len, seq_len.data_ptr(), err.data_ptr(),
+        k_new.data_ptr(), v_new.data_ptr(), n, q.data_ptr(), out.data_ptr(), wp, wb, _stream(stream)))
 
 
 def fullkv_verify_attn(d: Dims, k: torch.Tensor, v: torch.Tensor, seq_len: torch.Tensor,

@@ -11,7 +11,7 @@ using namespace masw;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxSplits = 1024;
+constexpr int kMaxSplits = 256;   // split partials merged by one work-group
 constexpr long kTargetWorkGroups = 512;   // two per CU on 256 CUs
 constexpr long kMinKeysPerSplit = 128;
 
@@ -47,14 +47,16 @@ int choose_splits(const masw_dims* d, long max_keys) {
 long masw_max_keys(const masw_dims* d) { return long(d->sink) + d->window + d->max_slots + 1; }
 
 struct WsPlan {
-  size_t flags, part_o, part_ml, total;
+  size_t flags, counters, part_o, part_ml, total;
 };
 
+// [per-sequence flags][per-(sequence, KV head) split tickets][partial o][partial max/sum]
 WsPlan plan_workspace(const masw_dims* d, int splits, int rows_per_seq) {
   WsPlan p;
   const size_t rows = size_t(d->batch) * rows_per_seq;
   p.flags = 0;
-  p.part_o = align_up(size_t(d->batch) * sizeof(int32_t));
+  p.counters = align_up(size_t(d->batch) * sizeof(int32_t));
+  p.part_o = p.counters + align_up(size_t(d->batch) * d->n_kv_heads * sizeof(int32_t));
   const size_t po = splits > 1 ? rows * splits * d->head_dim * sizeof(float) : 0;
   p.part_ml = p.part_o + align_up(po);
   const size_t pml = splits > 1 ? rows * splits * 2 * sizeof(float) : 0;
@@ -86,9 +88,33 @@ void fill_common(DecodeArgs& a, const masw_dims* d, int splits, void* ws, const 
   a.Hkv = d->n_kv_heads;
   a.n_splits = splits;
   a.scale_log2 = scale_log2(d);
+  a.qo_stride = long(d->n_q_heads) * d->head_dim;
   char* base = static_cast<char*>(ws);
+  a.counters = splits > 1 ? reinterpret_cast<int32_t*>(base + p.counters) : nullptr;
   a.part_o = splits > 1 ? reinterpret_cast<float*>(base + p.part_o) : nullptr;
   a.part_ml = splits > 1 ? reinterpret_cast<float*>(base + p.part_ml) : nullptr;
+}
+
+const void* or_else(const void* p, const void* q) { return p ? p : q; }
+
+// The three-segment memory of one layer as the decode kernel reads it.
+void fill_masw_memory(DecodeArgs& a, const masw_dims* d, const masw_layer* L) {
+  a.k[0] = or_else(L->k_sink, L->k_ring); a.k[1] = L->k_ring; a.k[2] = or_else(L->k_slot, L->k_ring);
+  a.v[0] = or_else(L->v_sink, L->v_ring); a.v[1] = L->v_ring; a.v[2] = or_else(L->v_slot, L->v_ring);
+  a.wk[0] = L->k_sink ? L->k_sink : L->k_ring; a.wk[1] = L->k_ring;
+  a.wv[0] = L->v_sink ? L->v_sink : L->v_ring; a.wv[1] = L->v_ring;
+  a.cap[0] = d->sink; a.cap[1] = d->window + d->interval; a.cap[2] = d->max_slots;
+  a.g = masw_geom(d);
+}
+
+// A full cache [B][Hkv][max_len][D] as a one-segment memory.
+void fill_full_memory(DecodeArgs& a, const void* k, const void* v, int32_t max_len) {
+  for (int s = 0; s < 3; ++s) { a.k[s] = k; a.v[s] = v; }
+  a.wk[0] = a.wk[1] = const_cast<void*>(k);
+  a.wv[0] = a.wv[1] = const_cast<void*>(v);
+  a.cap[0] = max_len; a.cap[1] = 0; a.cap[2] = 0;
+  a.g = full_geom(max_len);
+  a.max_len = max_len;
 }
 
 int check_layer(const masw_dims* d, const masw_layer* L) {
@@ -97,8 +123,6 @@ int check_layer(const masw_dims* d, const masw_layer* L) {
   if (d->max_slots > 0 && (!L->k_slot || !L->v_slot)) return MASW_ERR_ARG;
   return MASW_OK;
 }
-
-const void* or_else(const void* p, const void* q) { return p ? p : q; }
 
 }  // namespace
 
@@ -194,21 +218,28 @@ MASW_API int fullkv_append(const masw_dims* d, void* k, void* v, int32_t max_len
 
 MASW_API int masw_draft_attn(const masw_dims* d, const masw_layer* L, const masw_seq* seq, const void* q,
                              void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return masw_decode_step(d, L, seq, nullptr, nullptr, 0, q, out, ws, ws_bytes, stream);
+}
+
+MASW_API int masw_decode_step(const masw_dims* d, const masw_layer* L, const masw_seq* seq,
+                              const void* k_new, const void* v_new, int32_t n_new, const void* q,
+                              void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(d, true);
   if (st) return st;
   if ((st = check_layer(d, L))) return st;
-  if (!seq || !seq->seq_len || !seq->err || !q || !out) return MASW_ERR_ARG;
+  if (!seq || !seq->seq_len || !seq->err || !q || !out || n_new < 0) return MASW_ERR_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return MASW_ERR_ARG;
   const int splits = choose_splits(d, masw_max_keys(d));
   const WsPlan p = plan_workspace(d, splits, d->n_q_heads);
   if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
   DecodeArgs a{};
-  a.k[0] = or_else(L->k_sink, L->k_ring); a.k[1] = L->k_ring; a.k[2] = or_else(L->k_slot, L->k_ring);
-  a.v[0] = or_else(L->v_sink, L->v_ring); a.v[1] = L->v_ring; a.v[2] = or_else(L->v_slot, L->v_ring);
-  a.cap[0] = d->sink; a.cap[1] = d->window + d->interval; a.cap[2] = d->max_slots;
-  a.g = masw_geom(d);
+  fill_masw_memory(a, d, L);
   a.seq_len = seq->seq_len;
   a.err = seq->err;
   a.n_slots = L->n_slots;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.n_new = n_new;
   a.q = q;
   a.out = out;
   fill_common(a, d, splits, ws, p);
@@ -218,19 +249,27 @@ MASW_API int masw_draft_attn(const masw_dims* d, const masw_layer* L, const masw
 MASW_API int fullkv_decode_attn(const masw_dims* d, const void* k, const void* v, int32_t max_len,
                                 const int32_t* seq_len, int32_t* err, const void* q, void* out, void* ws,
                                 size_t ws_bytes, hipStream_t stream) {
+  return fullkv_decode_step(d, const_cast<void*>(k), const_cast<void*>(v), max_len, seq_len, err, nullptr,
+                            nullptr, 0, q, out, ws, ws_bytes, stream);
+}
+
+MASW_API int fullkv_decode_step(const masw_dims* d, void* k, void* v, int32_t max_len, const int32_t* seq_len,
+                                int32_t* err, const void* k_new, const void* v_new, int32_t n_new,
+                                const void* q, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(d, false);
   if (st) return st;
-  if (!k || !v || !seq_len || !err || !q || !out || max_len < 1) return MASW_ERR_ARG;
+  if (!k || !v || !seq_len || !err || !q || !out || max_len < 1 || n_new < 0) return MASW_ERR_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return MASW_ERR_ARG;
   const int splits = choose_splits(d, max_len);
   const WsPlan p = plan_workspace(d, splits, d->n_q_heads);
   if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
   DecodeArgs a{};
-  for (int s = 0; s < 3; ++s) { a.k[s] = k; a.v[s] = v; }
-  a.cap[0] = max_len; a.cap[1] = 0; a.cap[2] = 0;
-  a.g = full_geom(max_len);
+  fill_full_memory(a, k, v, max_len);
   a.seq_len = seq_len;
   a.err = err;
-  a.max_len = max_len;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.n_new = n_new;
   a.q = q;
   a.out = out;
   fill_common(a, d, splits, ws, p);
@@ -270,10 +309,7 @@ MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, cons
   if ((st = launch_project(pa, d->dtype, stream))) return st;
 
   DecodeArgs a{};
-  a.k[0] = or_else(L->k_sink, L->k_ring); a.k[1] = L->k_ring; a.k[2] = or_else(L->k_slot, L->k_ring);
-  a.v[0] = or_else(L->v_sink, L->v_ring); a.v[1] = L->v_ring; a.v[2] = or_else(L->v_slot, L->v_ring);
-  a.cap[0] = d->sink; a.cap[1] = d->window + d->interval; a.cap[2] = d->max_slots;
-  a.g = masw_geom(d);
+  fill_masw_memory(a, d, L);
   a.seq_len = seq->seq_len;
   a.err = seq->err;
   a.active = active;
@@ -292,8 +328,48 @@ MASW_API int fullkv_verify_attn(const masw_dims* d, const void* k, const void* v
   int st = check_dims(d, false);
   if (st) return st;
   if (!k || !v || !seq_len || !err || !q || !out || max_len < 1 || n_q < 1 || n_q > 16) return MASW_ERR_ARG;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return MASW_ERR_UNIMPLEMENTED;
+  const int splits = choose_splits(d, max_len);
+  const int rows = d->n_q_heads / d->n_kv_heads * n_q;
+  const WsPlan p = plan_workspace(d, splits, d->n_q_heads * n_q);
+  if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
+  char* base = static_cast<char*>(ws);
+  if (d->dtype == MASW_BF16 && d->head_dim == 128 && rows <= 64) {
+    VerifyArgs a{};
+    a.k = k;
+    a.v = v;
+    a.max_len = max_len;
+    a.seq_len = seq_len;
+    a.err = err;
+    a.q = q;
+    a.out = out;
+    a.counters = splits > 1 ? reinterpret_cast<int32_t*>(base + p.counters) : nullptr;
+    a.part_o = splits > 1 ? reinterpret_cast<float*>(base + p.part_o) : nullptr;
+    a.part_ml = splits > 1 ? reinterpret_cast<float*>(base + p.part_ml) : nullptr;
+    a.B = d->batch;
+    a.Hq = d->n_q_heads;
+    a.Hkv = d->n_kv_heads;
+    a.n_q = n_q;
+    a.n_splits = splits;
+    a.scale_log2 = scale_log2(d);
+    return launch_verify_mfma(a, stream);
+  }
+  // Other shapes: one vector-ALU decode pass per candidate, query j over keys 1..t-n_q+1+j.
+  const size_t esz = d->dtype == MASW_BF16 ? 2 : 4;
+  const size_t step = size_t(d->n_q_heads) * d->head_dim * esz;
+  for (int j = 0; j < n_q; ++j) {
+    DecodeArgs a{};
+    fill_full_memory(a, k, v, max_len);
+    a.seq_len = seq_len;
+    a.err = err;
+    a.back = n_q - 1 - j;
+    a.min_t = n_q;
+    fill_common(a, d, splits, ws, p);
+    a.q = static_cast<const char*>(q) + j * step;
+    a.out = static_cast<char*>(out) + j * step;
+    a.qo_stride = long(n_q) * d->n_q_heads * d->head_dim;
+    if ((st = launch_decode(a, d->dtype, d->head_dim, stream))) return st;
+  }
+  return MASW_OK;
 }
 
 MASW_API int masw_debug_keylist(const masw_dims* d, const masw_seq* seq, int32_t back, int32_t* out,

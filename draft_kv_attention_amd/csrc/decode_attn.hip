@@ -7,17 +7,26 @@
 //
 // Work decomposition (CDNA4, wave64):
 //   grid  = (splits, Hkv, B); each work-group owns one contiguous chunk of the logical
-//           key list of one (sequence, KV head) and 4 waves stride over it in tiles of
-//           32 keys.
-//   wave  = 4 rows of 16 lanes; a row holds one key: each lane loads D/16 elements of
-//           K and of V (16 B for bf16 D=128), so one load instruction moves 4 whole
-//           256-byte rows (coalesced).  q.k partial dots use v_dot2_f32_bf16 and are
-//           summed over the 16 lanes with DPP row rotations.
+//           key list of one (sequence, KV head); its 4 waves stride over the chunk in
+//           tiles of kDecodeTileKeys keys, optionally double-buffered (tile i+1 in
+//           flight while tile i is reduced).
+//   wave  = 64/LPR rows of LPR lanes; a row holds one key.  bf16: 8 lanes x 32 bytes
+//           per 256-byte row (D = 128), so a load instruction pair moves 8 whole rows;
+//           q.k partial dots use v_dot2_f32_bf16 and are summed over the 8 lanes with
+//           three DPP steps.  P.V also runs on v_dot2_f32_bf16: a lane pairs two of its
+//           rows (one v_perm_b32 per dword) and P is rounded to bf16 for that product,
+//           the usual flash-attention precision; the running sum l stays fp32.
+//           fp32 (small models): 16 lanes per row and plain FMAs.
 //   softmax is online (running max in log2 units, rescale per tile); waves merge
-//   through LDS, splits through a second small kernel (flash-decoding).
+//   through LDS; splits merge in the same launch: every work-group writes an
+//   (max, sum, o) partial and the last one to finish its (sequence, KV head) - found
+//   with an atomic ticket, reset to zero afterwards - merges them (flash-decoding
+//   without a second kernel).
 // Every key row is located through resolve_key(), which maps the logical index to
 // sink row i-1, ring row (i-S-1) mod (W+r) or slot row m-1 on the device, so no host
-// round trip is needed when t changes.
+// round trip is needed when t changes.  With a fused append the newest n_new raw
+// tokens are read straight from the caller's k_new/v_new and split 0 writes them into
+// the memory (rows no other work-group of this launch reads).
 #include "masw_internal.hpp"
 
 namespace masw {
@@ -25,22 +34,22 @@ namespace {
 
 // Keys of sequence b for this launch, or 0 when the sequence is skipped (device
 // error bits are reported once per sequence when `report`).
-__device__ __forceinline__ int decode_keys(const DecodeArgs& a, int b, KeySpan& ks, bool report) {
-  const int t = a.seq_len[b];
+__device__ __forceinline__ int decode_keys(const DecodeArgs& a, int t, int have, int act,
+                                           KeySpan& ks, bool report) {
   if (a.active) {  // slot query of masw_materialize_slot: gated by the boundary decision
-    if (a.active[b] <= 0) return 0;
+    if (act <= 0) return 0;
     ks = key_span(t - a.back, a.g);
     ks.nslot += a.self_slot;
     return ks.total();
   }
   const int tv = t - a.back;
   int bits = 0;
-  if (tv < 1 || (a.max_len > 0 && t > a.max_len)) {
+  if (tv < 1 || t < a.min_t || t < a.n_new || (a.max_len > 0 && t > a.max_len)) {
     bits = MASW_DEV_SEQ_RANGE;
   } else {
     ks = key_span(tv, a.g);
     if (ks.nslot > a.g.max_slots) bits = MASW_DEV_SLOT_CAPACITY;
-    else if (a.n_slots && a.n_slots[b] < ks.nslot) bits = MASW_DEV_SLOT_MISSING;
+    else if (a.n_slots && have < ks.nslot) bits = MASW_DEV_SLOT_MISSING;
   }
   if (bits) {
     if (report) atomicOr(a.err, bits);
@@ -56,24 +65,21 @@ __device__ __forceinline__ int split_chunk(int n, int n_splits) {
   return (c + kDecodeTileKeys - 1) / kDecodeTileKeys * kDecodeTileKeys;
 }
 
-template <int NW>
-__device__ __forceinline__ void load_frag(uint32_t (&w)[NW], const void* p) {
-  if constexpr (NW == 2) {
-    uint2 x = *reinterpret_cast<const uint2*>(p);
-    w[0] = x.x; w[1] = x.y;
-  } else if constexpr (NW == 4) {
-    uint4 x = *reinterpret_cast<const uint4*>(p);
-    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-  } else {
-    static_assert(NW == 8, "fragment size");
-    uint4 x = reinterpret_cast<const uint4*>(p)[0];
-    uint4 y = reinterpret_cast<const uint4*>(p)[1];
-    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-    w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
+// A lane fragment of one row: NW dwords in 16-byte chunks; chunk c sits CH elements
+// after chunk 0, so the LPR lanes of a row together cover each 128/256-byte span of the
+// row contiguously (one load instruction reads whole cache lines).
+template <int NW, int CH, typename T>
+__device__ __forceinline__ void load_frag(uint32_t (&w)[NW], const T* p) {
+  static_assert(NW % 4 == 0, "fragments are whole 16-byte chunks");
+#pragma unroll
+  for (int c = 0; c < NW / 4; ++c) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p + c * CH);
+    w[4 * c] = x.x; w[4 * c + 1] = x.y; w[4 * c + 2] = x.z; w[4 * c + 3] = x.w;
   }
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T, int NW>
 __device__ __forceinline__ float frag_dot(const uint32_t (&a)[NW], const uint32_t (&b)[NW]) {
@@ -97,39 +103,263 @@ __device__ __forceinline__ float frag_elem(const uint32_t (&w)[NW], int e) {
   else return __uint_as_float(w[e]);
 }
 
+// Fused append: copy the n_new new tokens of (b, kvh) into sink / ring rows.  An
+// eviction of a token whose block has no slot yet is suppressed and reported.
+template <typename T, int D>
+__device__ void append_rows(const DecodeArgs& a, int b, int kvh, int t, int have, bool report) {
+  if (t < a.n_new || (a.max_len > 0 && t > a.max_len)) return;   // reported by decode_keys
+  constexpr int VEC = 16 / int(sizeof(T));
+  constexpr int PKT = D / VEC;
+  const size_t unit = size_t(b) * a.Hkv + kvh;
+  int bits = 0;
+  for (int p = threadIdx.x; p < a.n_new * PKT; p += kDecodeThreads) {
+    const int j = p / PKT;
+    const int d = (p - j * PKT) * VEC;
+    const int i = t - a.n_new + 1 + j;
+    T* dk;
+    T* dv;
+    size_t off;
+    if (i <= a.g.S) {
+      off = (unit * a.cap[0] + (i - 1)) * D + d;
+      dk = static_cast<T*>(a.wk[0]);
+      dv = static_cast<T*>(a.wv[0]);
+    } else {
+      const int prev = i - a.g.C;
+      if (prev > a.g.S && have < (prev - a.g.S + a.g.r - 1) / a.g.r) {
+        bits |= MASW_DEV_PENDING_SLOT;
+        continue;
+      }
+      off = (unit * a.g.C + (i - a.g.S - 1) % a.g.C) * D + d;
+      dk = static_cast<T*>(a.wk[1]);
+      dv = static_cast<T*>(a.wv[1]);
+    }
+    const size_t src = ((size_t(b) * a.n_new + j) * a.Hkv + kvh) * D + d;
+    *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_new) + src);
+    *reinterpret_cast<uint4*>(dv + off) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_new) + src);
+  }
+  if (bits && report) atomicOr(a.err, bits);
+}
+
+constexpr int kMergeBatch = 16;   // split partials one thread loads at once
+constexpr int kMaxMergeSplits = 256;
+
+// Combine n_valid (max, sum, o) partials of the G query heads of one KV head into out.
+template <typename T, int D, int G>
+__device__ __forceinline__ void merge_partials(const float* part_o, const float* part_ml, size_t row0, int n_splits,
+                                               int n_valid, T* outb) {
+  __shared__ float sm_pm[G][kMaxMergeSplits], sm_pl[G][kMaxMergeSplits];
+  __shared__ float sm_M[G];
+  for (int i = threadIdx.x; i < G * n_valid; i += kDecodeThreads) {
+    const int g = i / n_valid, sp = i - (i / n_valid) * n_valid;
+    const float* ml = part_ml + ((row0 + g) * n_splits + sp) * 2;
+    sm_pm[g][sp] = load_partial(ml);
+    sm_pl[g][sp] = load_partial(ml + 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_valid; ++sp) M = fmaxf(M, sm_pm[threadIdx.x][sp]);
+    sm_M[threadIdx.x] = M;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+    const int g = idx / D, d = idx - (idx / D) * D;
+    const float* po = part_o + (row0 + g) * n_splits * D + d;
+    const float M = sm_M[g];
+    float L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < n_valid; s0 += kMergeBatch) {
+      float v[kMergeBatch];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) v[k] = s0 + k < n_valid ? load_partial(&po[size_t(s0 + k) * D]) : 0.f;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        if (s0 + k < n_valid) {
+          const float wt = fast_exp2(sm_pm[g][s0 + k] - M);
+          L = fmaf(wt, sm_pl[g][s0 + k], L);
+          O = fmaf(wt, v[k], O);
+        }
+      }
+    }
+    outb[g * D + d] = Elem<T>::from_f32(O / L);
+  }
+}
+
+// Lanes per key row: bf16 uses 8 lanes x 32 bytes (3 DPP steps per row reduction),
+// fp32 16 lanes.  A wave instruction then covers 64 / LPR rows.
+template <typename T> struct RowLayout { static constexpr int LPR = sizeof(T) == 2 ? 8 : 16; };
+
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+  if constexpr (LPR == 16) {
+    return row16_sum(v);
+  } else {
+    // quad xor 1, quad xor 2, then mirror inside the 8-lane half row
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false));
+    return v;
+  }
+}
+
+// Reduce across the 64 / LPR row groups of a wave (lanes equal modulo LPR).
+template <int LPR>
+__device__ __forceinline__ float groups_max(float v) {
+  if constexpr (LPR == 8) v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false)));
+  v = fmaxf(v, xor_lanes(v, 16));
+  return fmaxf(v, xor_lanes(v, 32));
+}
+template <int LPR>
+__device__ __forceinline__ float groups_sum(float v) {
+  if constexpr (LPR == 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+  v += xor_lanes(v, 16);
+  return v + xor_lanes(v, 32);
+}
+
+// Where a lane's rows live, as element offsets from the sink base of K (and of V): the
+// ring, slot and new-token blocks are separate allocations, so each is one 64-bit
+// delta.  Keeping them as plain values (no struct or array of pointers to index) lets
+// the per-row choice compile to v_cndmask instead of a table in scratch memory.
+struct TileSrc {
+  long dk_ring, dk_slot, dk_new, dv_ring, dv_slot, dv_new;
+  long new_row;
+  int t_old;
+};
+
+// Issue the loads of one tile: row u of this lane is logical key tile + u*RPI + lgrp.
+template <typename T, int D, int U, int NW, int CH, int RPI>
+__device__ __forceinline__ void load_tile(uint32_t (&fk)[U][NW], uint32_t (&fv)[U][NW], int tile, int k0, int k1,
+                                          int lgrp, const KeySpan& ks, const MemGeom& g, const T* kb0,
+                                          const T* vb0, const TileSrc src) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = tile + u * RPI + lgrp;
+    const KeyRef kr = resolve_key(j < k1 ? j : k0, ks, g);
+    const bool is_new = kr.seg != 2 && kr.id > src.t_old;
+    const long row = is_new ? long(kr.id - src.t_old - 1) * src.new_row : long(kr.row) * D;
+    const long dk = is_new ? src.dk_new : (kr.seg == 0 ? 0L : (kr.seg == 1 ? src.dk_ring : src.dk_slot));
+    const long dv = is_new ? src.dv_new : (kr.seg == 0 ? 0L : (kr.seg == 1 ? src.dv_ring : src.dv_slot));
+    load_frag<NW, CH>(fk[u], kb0 + dk + row);
+    load_frag<NW, CH>(fv[u], vb0 + dv + row);
+  }
+}
+
+// Online-softmax update of (m, l, acc) with one tile.
+template <typename T, int G, int U, int NW, int EPL, int LPR, int RPI>
+__device__ __forceinline__ void reduce_tile(const uint32_t (&fk)[U][NW], const uint32_t (&fv)[U][NW], int tile,
+                                            int k1, int lgrp, float scale_log2, const uint32_t (&qw)[G][NW],
+                                            float (&m)[G], float (&l)[G], float (&acc)[G][EPL]) {
+  float s[U][G];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool valid = tile + u * RPI + lgrp < k1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float d = row_sum<LPR>(frag_dot<T, NW>(qw[g], fk[u]));
+      s[u][g] = valid ? d * scale_log2 : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mt = s[0][g];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
+    mt = groups_max<LPR>(mt);                 // finite: row 0 of the tile is valid
+    const float mn = fmaxf(m[g], mt);
+    if (mn != m[g]) {                         // wave-uniform: rescale only when the max grew
+      const float alpha = fast_exp2(m[g] - mn); // 0 on the first tile (m = -inf)
+      m[g] = mn;
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = fast_exp2(s[u][g] - mn);
+      s[u][g] = p;
+      l[g] += p;
+    }
+  }
+  if constexpr (sizeof(T) == 2) {
+    // P.V on v_dot2_f32_bf16: two rows of this lane at once, P rounded to bf16.
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      uint32_t pp[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        pp[g] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{s[u][g], s[u + 1][g]}, bf16x2_t));
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t lo = __builtin_amdgcn_perm(fv[u + 1][w], fv[u][w], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(fv[u + 1][w], fv[u][w], 0x07060302u);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          acc[g][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp[g]),
+                                                          __builtin_bit_cast(bf16x2_t, lo), acc[g][2 * w], false);
+          acc[g][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp[g]),
+                                                              __builtin_bit_cast(bf16x2_t, hi), acc[g][2 * w + 1], false);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(s[u][g], frag_elem<T, NW>(fv[u], e), acc[g][e]);
+  }
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
-  constexpr int EPL = D / 16;                    // elements per lane of one row
+  constexpr int LPR = RowLayout<T>::LPR;
+  constexpr int RPI = kWave / LPR;               // rows per wave instruction
+  constexpr int EPL = D / LPR;                   // elements per lane of one row
   constexpr int NW = EPL * int(sizeof(T)) / 4;   // dwords per lane of one row
-  constexpr int U = kDecodeTileKeys / 4;         // rows per lane per tile
+  constexpr int VEC = 16 / int(sizeof(T));       // elements per 16-byte chunk
+  constexpr int CH = LPR * VEC;                  // elements between a lane's chunks
+  constexpr int U = kDecodeTileKeys / RPI;       // rows per lane per tile
   constexpr int NWAVES = kDecodeThreads / kWave;
+  constexpr int STRIDE = NWAVES * kDecodeTileKeys;
+  static_assert(U % 2 == 0, "rows are paired for the bf16 P.V dot products");
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int lrow = lane >> 4;
-  const int l16 = lane & 15;
+  const int lgrp = lane / LPR;
+  const int lsub = lane % LPR;
+
+  // Start-up loads are independent of each other: issue them together.
+  const int t = a.seq_len[b];
+  const int have = a.n_slots ? a.n_slots[b] : 0;
+  const int act = a.active ? a.active[b] : 1;
+  uint32_t qw[G][NW];
+  const T* qb = static_cast<const T*>(a.q) + size_t(b) * a.qo_stride + size_t(kvh) * G * D + lsub * VEC;
+#pragma unroll
+  for (int g = 0; g < G; ++g) load_frag<NW, CH>(qw[g], qb + g * D);
+
+  if (a.n_new > 0 && split == 0) append_rows<T, D>(a, b, kvh, t, have, kvh == 0);
 
   KeySpan ks;
-  const int n = decode_keys(a, b, ks, split == 0 && kvh == 0 && threadIdx.x == 0);
+  const int n = decode_keys(a, t, have, act, ks, split == 0 && kvh == 0 && threadIdx.x == 0);
   if (n == 0) return;
   const int chunk = split_chunk(n, a.n_splits);
   const int k0 = split * chunk;
   if (k0 >= n) return;
   const int k1 = min(k0 + chunk, n);
+  const int n_valid = (n + chunk - 1) / chunk;
 
   const size_t unit = size_t(b) * a.Hkv + kvh;
-  const T* kb0 = static_cast<const T*>(a.k[0]) + unit * a.cap[0] * D + l16 * EPL;
-  const T* kb1 = static_cast<const T*>(a.k[1]) + unit * a.cap[1] * D + l16 * EPL;
-  const T* kb2 = static_cast<const T*>(a.k[2]) + unit * a.cap[2] * D + l16 * EPL;
-  const T* vb0 = static_cast<const T*>(a.v[0]) + unit * a.cap[0] * D + l16 * EPL;
-  const T* vb1 = static_cast<const T*>(a.v[1]) + unit * a.cap[1] * D + l16 * EPL;
-  const T* vb2 = static_cast<const T*>(a.v[2]) + unit * a.cap[2] * D + l16 * EPL;
-
-  uint32_t qw[G][NW];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-    load_frag<NW>(qw[g], static_cast<const T*>(a.q) + (size_t(b) * a.Hq + kvh * G + g) * D + l16 * EPL);
+  const T* kb0 = static_cast<const T*>(a.k[0]) + unit * a.cap[0] * D + lsub * VEC;
+  const T* kb1 = static_cast<const T*>(a.k[1]) + unit * a.cap[1] * D + lsub * VEC;
+  const T* kb2 = static_cast<const T*>(a.k[2]) + unit * a.cap[2] * D + lsub * VEC;
+  const T* vb0 = static_cast<const T*>(a.v[0]) + unit * a.cap[0] * D + lsub * VEC;
+  const T* vb1 = static_cast<const T*>(a.v[1]) + unit * a.cap[1] * D + lsub * VEC;
+  const T* vb2 = static_cast<const T*>(a.v[2]) + unit * a.cap[2] * D + lsub * VEC;
+  const int t_old = t - a.n_new;   // positions above this come from k_new / v_new
+  const size_t new_row = size_t(a.Hkv) * D;
+  const T* knb = a.n_new ? static_cast<const T*>(a.k_new) + (size_t(b) * a.n_new * a.Hkv + kvh) * D + lsub * VEC : kb0;
+  const T* vnb = a.n_new ? static_cast<const T*>(a.v_new) + (size_t(b) * a.n_new * a.Hkv + kvh) * D + lsub * VEC : vb0;
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -140,72 +370,56 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  for (int tile = k0 + wave * kDecodeTileKeys; tile < k1; tile += NWAVES * kDecodeTileKeys) {
-    uint32_t kw[U][NW], vw[U][NW];
-    bool valid[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = tile + u * 4 + lrow;
-      valid[u] = j < k1;
-      const KeyRef kr = resolve_key(valid[u] ? j : k0, ks, a.g);
-      const size_t off = size_t(kr.row) * D;
-      const T* kp = kr.seg == 0 ? kb0 : (kr.seg == 1 ? kb1 : kb2);
-      const T* vp = kr.seg == 0 ? vb0 : (kr.seg == 1 ? vb1 : vb2);
-      load_frag<NW>(kw[u], kp + off);
-      load_frag<NW>(vw[u], vp + off);
+  const TileSrc src{long(kb1 - kb0), long(kb2 - kb0), long(knb - kb0), long(vb1 - vb0), long(vb2 - vb0),
+                     long(vnb - vb0), long(new_row), t_old};
+  if constexpr (kDecodeDoubleBuffer) {
+    uint32_t ka[U][NW], va[U][NW], kc[U][NW], vc[U][NW];
+    int tile = k0 + wave * kDecodeTileKeys;
+    if (tile < k1) load_tile<T, D, U, NW, CH, RPI>(ka, va, tile, k0, k1, lgrp, ks, a.g, kb0, vb0, src);
+    while (tile < k1) {
+      int nt = tile + STRIDE;
+      if (nt < k1) load_tile<T, D, U, NW, CH, RPI>(kc, vc, nt, k0, k1, lgrp, ks, a.g, kb0, vb0, src);
+      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, k1, lgrp, a.scale_log2, qw, m, l, acc);
+      tile = nt;
+      if (tile >= k1) break;
+      nt = tile + STRIDE;
+      if (nt < k1) load_tile<T, D, U, NW, CH, RPI>(ka, va, nt, k0, k1, lgrp, ks, a.g, kb0, vb0, src);
+      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(kc, vc, tile, k1, lgrp, a.scale_log2, qw, m, l, acc);
+      tile = nt;
     }
-    float s[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float d = row16_sum(frag_dot<T, NW>(qw[g], kw[u]));
-        s[u][g] = valid[u] ? d * a.scale_log2 : -INFINITY;
-      }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mt = s[0][g];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
-      mt = rows4_max(mt);                       // finite: row 0 of the tile is valid
-      const float mn = fmaxf(m[g], mt);
-      const float alpha = fast_exp2(m[g] - mn); // 0 on the first tile (m = -inf)
-      m[g] = mn;
-      l[g] *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float p = fast_exp2(s[u][g] - mn);
-        l[g] += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, frag_elem<T, NW>(vw[u], e), acc[g][e]);
-      }
+  } else {
+    uint32_t ka[U][NW], va[U][NW];
+    for (int tile = k0 + wave * kDecodeTileKeys; tile < k1; tile += STRIDE) {
+      load_tile<T, D, U, NW, CH, RPI>(ka, va, tile, k0, k1, lgrp, ks, a.g, kb0, vb0, src);
+      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, k1, lgrp, a.scale_log2, qw, m, l, acc);
     }
   }
 
-  // Rows of a wave share the running max; sum their partial l and o.
+  // Row groups of a wave share the running max; sum their partial l and o.
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    l[g] = rows4_sum(l[g]);
+    l[g] = groups_sum<LPR>(l[g]);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = rows4_sum(acc[g][e]);
+    for (int e = 0; e < EPL; ++e) acc[g][e] = groups_sum<LPR>(acc[g][e]);
   }
 
   __shared__ float sm_m[NWAVES][G], sm_l[NWAVES][G];
   __shared__ float sm_o[NWAVES][G][D];
+  __shared__ int sm_last;
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) { sm_m[wave][g] = m[g]; sm_l[wave][g] = l[g]; }
   }
-  if (lane < 16) {
+  if (lane < LPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave][g][l16 * EPL + e] = acc[g][e];
+      for (int e = 0; e < EPL; ++e) sm_o[wave][g][(e / VEC) * CH + lsub * VEC + e % VEC] = acc[g][e];
   }
   __syncthreads();
 
+  T* outb = static_cast<T*>(a.out) + size_t(b) * a.qo_stride + size_t(kvh) * G * D;
+  const size_t row0 = size_t(b) * a.Hq + size_t(kvh) * G;   // partial rows of this KV head
   for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
     const int g = idx / D, d = idx - (idx / D) * D;
     float M = sm_m[0][g];
@@ -218,27 +432,46 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       L = fmaf(wt, sm_l[w][g], L);
       O = fmaf(wt, sm_o[w][g][d], O);
     }
-    const size_t row = size_t(b) * a.Hq + kvh * G + g;
-    if (a.n_splits == 1) {
-      static_cast<T*>(a.out)[row * D + d] = Elem<T>::from_f32(O / L);
+    if (n_valid == 1) {
+      outb[g * D + d] = Elem<T>::from_f32(O / L);
     } else {
-      const size_t pr = row * a.n_splits + split;
-      a.part_o[pr * D + d] = O;
-      if (d == 0) { a.part_ml[pr * 2] = M; a.part_ml[pr * 2 + 1] = L; }
+      const size_t pr = (row0 + g) * a.n_splits + split;
+      store_partial(&a.part_o[pr * D + d], O);
+      if (d == 0) { store_partial(&a.part_ml[pr * 2], M); store_partial(&a.part_ml[pr * 2 + 1], L); }
     }
   }
-  if (a.n_splits == 1 && a.n_slots_out && kvh == 0 && threadIdx.x == 0) a.n_slots_out[b] = a.active[b];
+  if (n_valid == 1) {
+    if (a.n_slots_out && kvh == 0 && threadIdx.x == 0) a.n_slots_out[b] = act;
+    return;
+  }
+#if MASW_SPLIT_MERGE != 0
+  // Split merge: the last work-group of this (sequence, KV head) combines all partials.
+  // Every partial load is issued before any is used: (max, sum) pairs land in LDS,
+  // the o values of up to kMergeBatch splits per thread are in flight together.
+  if (!split_arrive(&a.counters[unit], n_valid, &sm_last)) return;
+  merge_partials<T, D, G>(a.part_o, a.part_ml, row0, a.n_splits, n_valid, outb);
+  if (threadIdx.x == 0) {
+    reset_ticket(&a.counters[unit]);
+    if (a.n_slots_out && kvh == 0) a.n_slots_out[b] = act;
+  }
+#else
+  (void)sm_last;
+#endif
 }
 
-// Merge the per-split (max, sum, o) partials of one (sequence, query head).
+// Separate merge pass (MASW_SPLIT_MERGE 0): one work-group per (query head, sequence).
 template <typename T, int D>
 __global__ __launch_bounds__(D) void combine_kernel(const DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int t = a.seq_len[b];
+  const int have = a.n_slots ? a.n_slots[b] : 0;
+  const int act = a.active ? a.active[b] : 1;
   KeySpan ks;
-  const int n = decode_keys(a, b, ks, false);
+  const int n = decode_keys(a, t, have, act, ks, false);
   if (n == 0) return;
   const int chunk = split_chunk(n, a.n_splits);
   const int nv = (n + chunk - 1) / chunk;
+  if (nv == 1) return;   // written directly by the single work-group
   const size_t row = size_t(b) * a.Hq + h;
   const float* ml = a.part_ml + row * a.n_splits * 2;
   const float* po = a.part_o + row * a.n_splits * D + d;
@@ -250,8 +483,8 @@ __global__ __launch_bounds__(D) void combine_kernel(const DecodeArgs a) {
     L = fmaf(wt, ml[2 * s + 1], L);
     O = fmaf(wt, po[size_t(s) * D], O);
   }
-  static_cast<T*>(a.out)[row * D + d] = Elem<T>::from_f32(O / L);
-  if (a.n_slots_out && h == 0 && d == 0) a.n_slots_out[b] = a.active[b];
+  static_cast<T*>(a.out)[size_t(b) * a.qo_stride + size_t(h) * D + d] = Elem<T>::from_f32(O / L);
+  if (a.n_slots_out && h == 0 && d == 0) a.n_slots_out[b] = act;
 }
 
 __global__ void keylist_kernel(const MemGeom g, const int32_t* seq_len, int back, int32_t* out,
@@ -278,8 +511,9 @@ __global__ void keylist_kernel(const MemGeom g, const int32_t* seq_len, int back
 template <typename T, int D, int G>
 int launch_typed(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(a.n_splits, a.Hkv, a.B), dim3(kDecodeThreads), 0, s, a);
-  if (a.n_splits > 1)
-    hipLaunchKernelGGL((combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(D), 0, s, a);
+#if MASW_SPLIT_MERGE == 0
+  if (a.n_splits > 1) hipLaunchKernelGGL((combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(D), 0, s, a);
+#endif
   return hipGetLastError() == hipSuccess ? MASW_OK : MASW_ERR_LAUNCH;
 }
 

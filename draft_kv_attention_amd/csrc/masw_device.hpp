@@ -68,6 +68,64 @@ __device__ __forceinline__ float rows4_sum(float v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
+// Split merge inside one launch (flash-decoding without a second kernel)
+// ---------------------------------------------------------------------------
+// Each work-group of a (sequence, KV head) publishes an (max, sum, o) partial and
+// takes a ticket; the last arrival merges.  On a multi-XCD part a device-scope
+// __threadfence() writes back and invalidates the whole L2 of the issuing XCD, which
+// costs far more than the partials themselves when every work-group does it.  The
+// partials are therefore written and read with agent-scope relaxed atomics (per-access
+// write-through / L2-bypassing, coherent across XCDs), the writer waits for its stores
+// to complete (s_waitcnt vmcnt(0)) before the ticket is taken, and the reader loads
+// only after the ticket told it everyone else had arrived.
+//   MASW_SPLIT_MERGE 2: that protocol (default);
+//   MASW_SPLIT_MERGE 1: plain stores/loads with __threadfence() around the ticket;
+//   MASW_SPLIT_MERGE 0: no in-launch merge, a separate combine kernel follows.
+#ifndef MASW_SPLIT_MERGE
+#define MASW_SPLIT_MERGE 2
+#endif
+
+__device__ __forceinline__ void store_partial(float* p, float v) {
+#if MASW_SPLIT_MERGE == 2
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  *p = v;
+#endif
+}
+
+__device__ __forceinline__ float load_partial(const float* p) {
+#if MASW_SPLIT_MERGE == 2
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  return *p;
+#endif
+}
+
+// Called by every thread of the work-group after its partial stores; true (for the
+// whole work-group) when this is the last of n_valid arrivals.  The last arrival
+// resets the counter with reset_ticket() once it has merged.
+__device__ __forceinline__ bool split_arrive(int32_t* counter, int n_valid, int* sm_flag) {
+#if MASW_SPLIT_MERGE == 1
+  __threadfence();
+#else
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
+#endif
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *sm_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_valid - 1;
+  __syncthreads();
+  const bool last = *sm_flag != 0;
+#if MASW_SPLIT_MERGE == 1
+  if (last) __threadfence();
+#endif
+  return last;
+}
+
+__device__ __forceinline__ void reset_ticket(int32_t* counter) {
+  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // Memory geometry and the key resolver (Technical Review §3.1, Eq. 4)
 // ---------------------------------------------------------------------------
 struct MemGeom {

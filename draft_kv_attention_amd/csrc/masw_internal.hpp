@@ -9,12 +9,22 @@
 
 namespace masw {
 
-// Keys per wave iteration of the decode kernel: 4 rows of 16 lanes x 8 rows per lane.
-constexpr int kDecodeTileKeys = 32;
+// Keys per wave iteration of the decode kernel, and whether a wave keeps the next
+// tile's loads in flight while it reduces the current one.
+#ifndef MASW_DECODE_TILE_KEYS
+#define MASW_DECODE_TILE_KEYS 32
+#endif
+#ifndef MASW_DECODE_DOUBLE_BUFFER
+#define MASW_DECODE_DOUBLE_BUFFER 0
+#endif
+constexpr int kDecodeTileKeys = MASW_DECODE_TILE_KEYS;
+constexpr bool kDecodeDoubleBuffer = MASW_DECODE_DOUBLE_BUFFER != 0;
 constexpr int kDecodeThreads = 256;
 
 // Split-K decode attention over one memory (three segments; a full cache is the sink
-// segment alone).  One work-group per (split, KV head, sequence).
+// segment alone).  One work-group per (split, KV head, sequence).  With several splits
+// each work-group writes an (max, sum, o) partial and the last one to finish a
+// (sequence, KV head) merges them, using a counter that it resets to zero.
 struct DecodeArgs {
   const void* k[3];   // segment bases: sink, ring, slot
   const void* v[3];
@@ -28,8 +38,18 @@ struct DecodeArgs {
   int back;                 // keys of keylist(t - back)
   int self_slot;            // slot-query mode: also attend to the new slot itself
   int max_len;              // full cache: t must not exceed it (0: no bound)
-  const void* q;            // [B][Hq][D]
-  void* out;                // [B][Hq][D]
+  int min_t;                // t below this is out of range (besides t - back >= 1)
+  // Fused append (n_new > 0): positions t-n_new+1..t are read from k_new/v_new
+  // ([B][n_new][Hkv][D]) and written into the memory by split 0 of each KV head.
+  const void* k_new;
+  const void* v_new;
+  int n_new;
+  void* wk[2];              // write bases: sink (or the full cache), ring
+  void* wv[2];
+  int32_t* counters;        // [B*Hkv] split-merge tickets, zero between calls
+  const void* q;            // q + b*qo_stride + h*D
+  void* out;                // out + b*qo_stride + h*D
+  long qo_stride;           // elements between sequences in q/out
   float* part_o;            // [B][Hq][splits][D]
   float* part_ml;           // [B][Hq][splits][2]  (running max in log2 units, sum)
   int B, Hq, Hkv, n_splits;
@@ -71,5 +91,23 @@ struct ProjectArgs {
 };
 
 int launch_project(const ProjectArgs& a, int dtype, hipStream_t s);
+
+// Multi-query verifier attention over a full cache on the matrix cores (bf16, D=128,
+// Hq/Hkv * n_q <= 64 rows per KV head).  Same partial/merge protocol as DecodeArgs.
+struct VerifyArgs {
+  const void* k; const void* v;   // [B][Hkv][max_len][D]
+  int max_len;
+  const int32_t* seq_len;
+  int32_t* err;
+  const void* q;                  // [B][n_q][Hq][D]
+  void* out;
+  int32_t* counters;
+  float* part_o;                  // [B][n_q*Hq][splits][D]
+  float* part_ml;
+  int B, Hq, Hkv, n_q, n_splits;
+  float scale_log2;
+};
+
+int launch_verify_mfma(const VerifyArgs& a, hipStream_t s);
 
 }  // namespace masw

@@ -1,0 +1,361 @@
+// verify_attn.hip - verifier attention over the full cache on the matrix cores
+// (Technical Review §3.3, Algorithm 2 step 5: the target checks the L_draft candidates
+// in one parallel pass over its own, uncompressed KV).
+//
+// n_q candidate queries sit at positions t-n_q+1 .. t; query j attends to keys
+// 1 .. t-n_q+1+j.  Per (sequence, KV head) the G query heads times n_q candidates form
+// R = G * n_q <= 64 rows (24 for a 32/8-head layer, 48 for 64/8), in NB = ceil(R/32)
+// blocks of 32.  With 24-48 FLOP per byte the vector ALUs cannot keep pace with HBM, so
+// both products run on v_mfma_f32_32x32x16_bf16:
+//   S^T[key][row] = K[key][d] . Q^T[d][row]       (A = K rows, B = Q rows, both from LDS)
+//   O^T[d][row]  += V^T[d][key] . P^T[key][row]   (A = V read transposed from LDS,
+//                                                  B = P straight from the S^T registers)
+// The transposed products make the accumulator lane own one query row, so the
+// online-softmax rescale is a per-lane scalar and P never leaves registers: the S^T
+// layout (lane = row, registers = keys) is the B-operand layout the second product
+// needs, with its 32 keys taken in the order the registers hold them.
+//
+// Work-group = 4 waves over one (split, KV head, sequence).  Per iteration the whole
+// work-group stages a tile of 32*4/NB keys of K and V in LDS (272-byte padded rows:
+// conflict-free 16-byte row reads and 2-byte column reads); wave w owns row block
+// w / (4/NB) and the 32-key slice w % (4/NB) of the tile, so each wave keeps one 64-float
+// O^T accumulator.  The next tile's global loads are issued into registers before the
+// current tile is computed.  Waves sharing a row block merge through LDS in a fixed
+// order; splits merge in the same launch through the last-arriving work-group.
+#include "masw_internal.hpp"
+
+namespace masw {
+namespace {
+
+constexpr int kVWaves = 4;
+constexpr int kVThreads = kVWaves * kWave;
+constexpr int kRS = 136;       // LDS row stride in bf16 elements (272 bytes)
+constexpr int kD = 128;
+constexpr int kMaxRows = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Native clang vector (not HIP's uint4 struct) so staging arrays stay in registers.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int NB> struct VTile {
+  static constexpr int WPR = kVWaves / NB;      // waves per row block
+  static constexpr int TK = 32 * WPR;           // keys per work-group tile
+  static constexpr int PER_THREAD = TK * 16 / kVThreads;   // 16-byte K chunks per thread
+};
+
+__device__ __forceinline__ int verify_chunk(int n, int n_splits, int tk) {
+  int c = (n + n_splits - 1) / n_splits;
+  return (c + tk - 1) / tk * tk;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// Global K/V rows of one tile into registers: 16 lanes per 256-byte row.
+template <int PT>
+__device__ __forceinline__ void fetch_tile(u32x4_t (&kr)[PT], u32x4_t (&vr)[PT], const uint16_t* kbase,
+                                           const uint16_t* vbase, int tile, int k1) {
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int c = i * kVThreads + threadIdx.x;   // chunk id inside the tile
+    const int key = min(tile + (c >> 4), k1 - 1);
+    kr[i] = *reinterpret_cast<const u32x4_t*>(kbase + size_t(key) * kD + (c & 15) * 8);
+    vr[i] = *reinterpret_cast<const u32x4_t*>(vbase + size_t(key) * kD + (c & 15) * 8);
+  }
+}
+
+template <int PT>
+__device__ __forceinline__ void stage_tile(const u32x4_t (&kr)[PT], const u32x4_t (&vr)[PT], uint16_t* Kt, uint16_t* Vt) {
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int c = i * kVThreads + threadIdx.x;
+    *reinterpret_cast<u32x4_t*>(Kt + (c >> 4) * kRS + (c & 15) * 8) = kr[i];
+    *reinterpret_cast<u32x4_t*>(Vt + (c >> 4) * kRS + (c & 15) * 8) = vr[i];
+  }
+}
+
+// Combine n_valid (max, sum, o) partials of the R rows of one KV head into out.  All
+// loads of a batch of splits are issued before any is used.
+__device__ __forceinline__ void merge_verify_partials(const VerifyArgs& a, int b, int kvh, int R, int n_valid) {
+  constexpr int kBatch = 16;
+  __shared__ float sm_M[kMaxRows];
+  const int G = a.Hq / a.Hkv;
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  if (threadIdx.x < R) {
+    const int row = threadIdx.x;
+    const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
+    const size_t prow = (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
+    const float* ml = a.part_ml + prow * a.n_splits * 2;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < n_valid; s0 += kBatch) {
+      float mm[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) mm[k] = s0 + k < n_valid ? load_partial(&ml[2 * (s0 + k)]) : -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mm[k]);
+    }
+    sm_M[row] = M;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < R * kD; idx += kVThreads) {
+    const int row = idx / kD, d = idx - (idx / kD) * kD;
+    const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
+    const size_t prow = (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
+    const float* ml = a.part_ml + prow * a.n_splits * 2;
+    const float* po = a.part_o + prow * a.n_splits * kD + d;
+    const float M = sm_M[row];
+    float L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < n_valid; s0 += kBatch) {
+      float v[kBatch], mm[kBatch], ll[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const bool in = s0 + k < n_valid;
+        v[k] = in ? load_partial(&po[size_t(s0 + k) * kD]) : 0.f;
+        mm[k] = in ? load_partial(&ml[2 * (s0 + k)]) : -INFINITY;
+        ll[k] = in ? load_partial(&ml[2 * (s0 + k) + 1]) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float w = fast_exp2(mm[k] - M);   // splits past a row's causal limit carry -inf
+        L = fmaf(w, ll[k], L);
+        O = fmaf(w, v[k], O);
+      }
+    }
+    out[prow * kD + d] = f32_to_bf16(O / L);
+  }
+}
+
+template <int NB>
+__global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyArgs a) {
+  constexpr int WPR = VTile<NB>::WPR;
+  constexpr int TK = VTile<NB>::TK;
+  constexpr int PT = VTile<NB>::PER_THREAD;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int rb = wave / WPR;                  // row block of this wave
+  const int kslice = (wave % WPR) * 32;       // key slice of this wave inside a tile
+  const int G = a.Hq / a.Hkv;
+  const int R = G * a.n_q;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[NB * 32 * kRS];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * TK * kRS];
+  __shared__ int sm_last;
+  uint16_t* Kt = sKV;
+  uint16_t* Vt = sKV + TK * kRS;
+
+  const int t = a.seq_len[b];
+  // Q rows of this KV head into LDS (rows >= R are zero).
+  for (int c = threadIdx.x; c < NB * 32 * 16; c += kVThreads) {
+    const int row = c >> 4, ch = c & 15;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row < R) {
+      const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
+      v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) +
+                                            ((size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g) * kD + ch * 8);
+    }
+    *reinterpret_cast<u32x4_t*>(sQ + row * kRS + ch * 8) = v;
+  }
+  if (t < a.n_q || t > a.max_len) {
+    if (split == 0 && kvh == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SEQ_RANGE);
+    return;
+  }
+  const int n = t;
+  const int chunk = verify_chunk(n, a.n_splits, TK);
+  const int k0 = split * chunk;
+  if (k0 >= n) return;
+  const int k1 = min(k0 + chunk, n);
+  const int n_valid = (n + chunk - 1) / chunk;
+
+  // causal limit of this lane's row: last key row (0-based) query j may see
+  const int rho = rb * 32 + l32;
+  const int lim = rho < R ? t - a.n_q + (rho - (rho / a.n_q) * a.n_q) : -1;
+
+  const size_t unit = size_t(b) * a.Hkv + kvh;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + unit * a.max_len * kD;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + unit * a.max_len * kD;
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  u32x4_t kr[PT], vr[PT];
+  fetch_tile<PT>(kr, vr, kbase, vbase, k0, k1);
+  for (int tile = k0; tile < k1; tile += TK) {
+    __syncthreads();                  // previous tile fully consumed (and Q staged)
+    stage_tile<PT>(kr, vr, Kt, Vt);
+    __syncthreads();
+    if (tile + TK < k1) fetch_tile<PT>(kr, vr, kbase, vbase, tile + TK, k1);   // next tile in flight
+
+    const int key0 = tile + kslice;
+    if (key0 < k1) {
+      f32x16_t s;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(Kt + (kslice + l32) * kRS + ks * 16 + half * 8);
+        const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(sQ + (rb * 32 + l32) * kRS + ks * 16 + half * 8);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
+                                                    __builtin_bit_cast(bf16x8_t, bq), s, 0, 0, 0);
+      }
+      // S^T layout: register v holds key 8*(v/4) + 4*half + v%4 of the slice, row l32.
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + 8 * (v >> 2) + 4 * half + (v & 3);
+        const float sc = (key < k1 && key <= lim) ? s[v] * a.scale_log2 : -INFINITY;
+        s[v] = sc;
+        tmax = fmaxf(tmax, sc);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float mn = fmaxf(m, tmax);
+      const float mref = mn == -INFINITY ? 0.f : mn;   // a row may have no key in this slice
+      const float alpha = fast_exp2(m - mref);
+      if (__any(mn != m)) {          // rescale only when some row's max grew
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      }
+      m = mn;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(s[v] - mref);
+        s[v] = p;
+        l += p;
+      }
+      // O^T += V^T P^T, two k-steps of 16 keys in register order.
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+        const int v0 = 8 * step;
+        const u32x4_t pb = {pack_bf16x2(s[v0 + 0], s[v0 + 1]), pack_bf16x2(s[v0 + 2], s[v0 + 3]),
+                            pack_bf16x2(s[v0 + 4], s[v0 + 5]), pack_bf16x2(s[v0 + 6], s[v0 + 7])};
+        const int kb = kslice + 16 * step + 4 * half;   // keys kb..kb+3, kb+8..kb+11
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const uint16_t* vc = Vt + db * 32 + l32;
+          const u32x4_t af = {uint32_t(vc[(kb + 0) * kRS]) | (uint32_t(vc[(kb + 1) * kRS]) << 16),
+                              uint32_t(vc[(kb + 2) * kRS]) | (uint32_t(vc[(kb + 3) * kRS]) << 16),
+                              uint32_t(vc[(kb + 8) * kRS]) | (uint32_t(vc[(kb + 9) * kRS]) << 16),
+                              uint32_t(vc[(kb + 10) * kRS]) | (uint32_t(vc[(kb + 11) * kRS]) << 16)};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
+                                                          __builtin_bit_cast(bf16x8_t, pb), o[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Keys of a row are split between lanes l32 and l32 + 32: total their sums.
+  l += __shfl_xor(l, 32, kWave);
+
+  // Merge the waves of each row block in a fixed order through LDS (reusing the tiles).
+  __syncthreads();
+  float* sm_ml = reinterpret_cast<float*>(sKV);          // [waves][32 rows][2]
+  float* sm_o = sm_ml + kVWaves * 32 * 2;                 // [NB*32 rows][128]
+  if (half == 0) {
+    sm_ml[(wave * 32 + l32) * 2] = m;
+    sm_ml[(wave * 32 + l32) * 2 + 1] = l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < WPR; ++w) M = fmaxf(M, sm_ml[((rb * WPR + w) * 32 + l32) * 2]);
+  const float wt = fast_exp2(m - (M == -INFINITY ? 0.f : M));
+  for (int w = 0; w < WPR; ++w) {
+    if (wave % WPR == w) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int idx = (rb * 32 + l32) * kD + db * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          const float val = wt * o[db][v];
+          sm_o[idx] = w == 0 ? val : sm_o[idx] + val;
+        }
+    }
+    __syncthreads();
+  }
+
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  for (int idx = threadIdx.x; idx < R * kD; idx += kVThreads) {
+    const int row = idx / kD, d = idx - (idx / kD) * kD;
+    const int rblk = row >> 5, r32 = row & 31;
+    const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
+    const size_t prow = (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
+    float Mr = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) Mr = fmaxf(Mr, sm_ml[((rblk * WPR + w) * 32 + r32) * 2]);
+    const float Mrr = Mr == -INFINITY ? 0.f : Mr;
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w)
+      L = fmaf(fast_exp2(sm_ml[((rblk * WPR + w) * 32 + r32) * 2] - Mrr), sm_ml[((rblk * WPR + w) * 32 + r32) * 2 + 1], L);
+    const float O = sm_o[row * kD + d];
+    if (n_valid == 1) {
+      out[prow * kD + d] = f32_to_bf16(O / L);
+    } else {
+      const size_t pr = prow * a.n_splits + split;
+      store_partial(&a.part_o[pr * kD + d], O);
+      if (d == 0) { store_partial(&a.part_ml[pr * 2], Mr); store_partial(&a.part_ml[pr * 2 + 1], L); }
+    }
+  }
+  if (n_valid == 1) return;
+#if MASW_SPLIT_MERGE != 0
+  if (!split_arrive(&a.counters[unit], n_valid, &sm_last)) return;
+  merge_verify_partials(a, b, kvh, R, n_valid);
+  if (threadIdx.x == 0) reset_ticket(&a.counters[unit]);
+#else
+  (void)sm_last;
+#endif
+}
+
+// Separate merge pass (MASW_SPLIT_MERGE 0): one work-group per (row, sequence).
+__global__ __launch_bounds__(kD) void verify_combine_kernel(const VerifyArgs a, int tk) {
+  const int r = blockIdx.x, b = blockIdx.y, d = threadIdx.x;   // r = j * Hq + h
+  const int t = a.seq_len[b];
+  if (t < a.n_q || t > a.max_len) return;
+  const int chunk = verify_chunk(t, a.n_splits, tk);
+  const int nv = (t + chunk - 1) / chunk;
+  if (nv == 1) return;
+  const size_t prow = size_t(b) * a.n_q * a.Hq + r;
+  const float* ml = a.part_ml + prow * a.n_splits * 2;
+  const float* po = a.part_o + prow * a.n_splits * kD + d;
+  float M = -INFINITY;
+  for (int s = 0; s < nv; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < nv; ++s) {
+    const float w = fast_exp2(ml[2 * s] - M);
+    L = fmaf(w, ml[2 * s + 1], L);
+    O = fmaf(w, po[size_t(s) * kD], O);
+  }
+  static_cast<uint16_t*>(a.out)[prow * kD + d] = f32_to_bf16(O / L);
+}
+
+}  // namespace
+
+int launch_verify_mfma(const VerifyArgs& a, hipStream_t s) {
+  const int rows = a.Hq / a.Hkv * a.n_q;
+  int tk;
+  if (rows <= 32) {
+    hipLaunchKernelGGL(verify_kernel<1>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
+    tk = VTile<1>::TK;
+  } else if (rows <= kMaxRows) {
+    hipLaunchKernelGGL(verify_kernel<2>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
+    tk = VTile<2>::TK;
+  } else {
+    return MASW_ERR_SHAPE;
+  }
+#if MASW_SPLIT_MERGE == 0
+  if (a.n_splits > 1)
+    hipLaunchKernelGGL(verify_combine_kernel, dim3(a.n_q * a.Hq, a.B), dim3(kD), 0, s, a, tk);
+#else
+  (void)tk;
+#endif
+  return hipGetLastError() == hipSuccess ? MASW_OK : MASW_ERR_LAUNCH;
+}
+
+}  // namespace masw

@@ -33,7 +33,10 @@
  *    bfloat16 bit patterns; results are rounded to nearest-even.  Accumulation is fp32.
  *  - Workspace: ops that split the key range (flash-decoding split-K) need a scratch
  *    buffer of at least masw_workspace_bytes(...) bytes, 256-byte aligned, that no other
- *    call uses concurrently.  Its contents need no initialization.
+ *    call uses concurrently.  The caller zero-fills it once after allocating it; every
+ *    call leaves the ticket counters it uses back at zero, so no later clearing is
+ *    needed (the split merge happens in the same launch: the last work-group of each
+ *    (sequence, KV head) combines the partials).
  */
 #ifndef MASW_H_
 #define MASW_H_
@@ -47,7 +50,7 @@ extern "C" {
 #endif
 
 #define MASW_API __attribute__((visibility("default")))
-#define MASW_ABI_VERSION 1
+#define MASW_ABI_VERSION 2
 
 /* ---- host status codes ------------------------------------------------------- */
 enum {
@@ -87,7 +90,7 @@ typedef struct {
   int32_t dtype;       /* masw_dtype of every K/V/q/out/h/w tensor                 */
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(D) ([TR] §2.3 Eq. 2)  */
   int32_t num_splits;  /* split-K plan: 0 = library heuristic, else splits per
-                          (sequence, KV head) in 1..1024.  Two calls over the same
+                          (sequence, KV head) in 1..256.  Two calls over the same
                           keys with the same value give bitwise equal results.     */
 } masw_dims;
 
@@ -162,6 +165,17 @@ MASW_API int masw_draft_attn(const masw_dims* dims, const masw_layer* layer,
                              const masw_seq* seq, const void* q, void* out, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* Fused decode step: masw_evict_append(k_new, v_new, n_new) followed by
+ * masw_draft_attn, in one launch.  The n_new newest keys are read straight from
+ * k_new/v_new while split 0 of each KV head writes them into the memory (same placement
+ * and legality rule as masw_evict_append; an illegal eviction is reported and not
+ * written, and the query still sees the new token).  n_new == 0 is masw_draft_attn.
+ * t < n_new: MASW_DEV_SEQ_RANGE, nothing written. */
+MASW_API int masw_decode_step(const masw_dims* dims, const masw_layer* layer, const masw_seq* seq,
+                              const void* k_new, const void* v_new, int32_t n_new, const void* q,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* Full-KV draft decode attention, the baseline ([TR] §2.3 Eq. 2 over K_{<=t}).
  * k, v [B][Hkv][max_len][D] (row i-1 holds position i); q, out [B][Hq][D]; keys 1..t.
  * Runs the same kernel as masw_draft_attn with a one-segment memory, so for
@@ -179,10 +193,19 @@ MASW_API int fullkv_append(const masw_dims* dims, void* k, void* v, int32_t max_
                            const int32_t* seq_len, int32_t* err, const void* k_new,
                            const void* v_new, int32_t n_new, hipStream_t stream);
 
+/* Fused full-KV decode step: fullkv_append then fullkv_decode_attn in one launch
+ * (the new rows are read from k_new/v_new and written by split 0). */
+MASW_API int fullkv_decode_step(const masw_dims* dims, void* k, void* v, int32_t max_len,
+                                const int32_t* seq_len, int32_t* err, const void* k_new,
+                                const void* v_new, int32_t n_new, const void* q, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Verifier attention over the full cache ([TR] §3.3 Algorithm 2 step 5): n_q candidate
  * positions checked in one parallel pass.  q, out [B][n_q][Hq][D]; query j sits at
  * position t-n_q+1+j (t = seq_len[b], the candidates already appended) and attends to
- * keys 1 .. t-n_q+1+j (causal among the candidates).  1 <= n_q <= 16.
+ * keys 1 .. t-n_q+1+j (causal among the candidates).  1 <= n_q <= 16.  bf16 with D = 128
+ * and (Hq/Hkv)*n_q <= 64 runs on the matrix cores; other shapes run one vector-ALU
+ * decode pass per candidate.
  * t < n_q or t > max_len: MASW_DEV_SEQ_RANGE, output untouched. */
 MASW_API int fullkv_verify_attn(const masw_dims* dims, const void* k, const void* v,
                                 int32_t max_len, const int32_t* seq_len, int32_t* err,

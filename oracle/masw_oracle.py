@@ -173,12 +173,13 @@ def project_slot(h: np.ndarray, w_k: np.ndarray, w_v: np.ndarray, n_kv_heads: in
                  head_dim: int, bf16_cache: bool) -> Tuple[np.ndarray, np.ndarray]:
     """K_g = H_g W_K,g and V_g = H_g W_V,g (row vector H, W [hidden][Hkv*D]).
 
-    KV head k is the column block k*D .. k*D+D-1.  Returns [Hkv][D] each, rounded to
-    bf16 when the cache stores bf16.
+    KV head k is the column block k*D .. k*D+D-1.  h may carry leading batch axes;
+    returns [..., Hkv, D] each, rounded to bf16 when the cache stores bf16.
     """
     h = np.asarray(h, np.float64)
-    kg = (h @ np.asarray(w_k, np.float64)).reshape(n_kv_heads, head_dim)
-    vg = (h @ np.asarray(w_v, np.float64)).reshape(n_kv_heads, head_dim)
+    lead = h.shape[:-1]
+    kg = (h @ np.asarray(w_k, np.float64)).reshape(lead + (n_kv_heads, head_dim))
+    vg = (h @ np.asarray(w_v, np.float64)).reshape(lead + (n_kv_heads, head_dim))
     if bf16_cache:
         kg, vg = to_bf16(kg), to_bf16(vg)
     return kg, vg
@@ -233,7 +234,18 @@ class DraftMemory:
         m = self.pending_boundary()
         if not m:
             return None
-        self.slots[m] = project_slot(h, w_k, w_v, self.Hkv, self.D, self.bf16)
+        kg, vg = project_slot(h, w_k, w_v, self.Hkv, self.D, self.bf16)
+        self.add_slot(m, kg, vg)
+        return self.slot_query(m, q_slot, scale, include_self)
+
+    def add_slot(self, m: int, kg: np.ndarray, vg: np.ndarray) -> None:
+        """Append g_m's K/V ([Hkv][D] each) to the slot chain (Algorithm 1 step 4)."""
+        if m != len(self.slots) + 1:
+            raise ValueError(f"slot {m} out of order (have {len(self.slots)})")
+        self.slots[m] = (np.asarray(kg, np.float64), np.asarray(vg, np.float64))
+
+    def slot_query(self, m: int, q_slot: np.ndarray, scale: float, include_self: bool = False) -> np.ndarray:
+        """g_m's query under the structured mask (Algorithm 1 step 2, reading R1)."""
         keys = slot_query_keylist(m, self.S, self.W, self.r, include_self)
         K, V = self.gather(keys)
         return gqa_attend(np.asarray(q_slot, np.float64), K, V, scale)

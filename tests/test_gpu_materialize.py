@@ -1,0 +1,128 @@
+"""GPU parity of slot materialization along the 512-boundary chain at 3B shapes, and of
+the draft attention at the bench's full size and launch configuration (sampled rows).
+
+The chain: batch 4, S=4, W=2048, r=64, one layer; 64 seeded raw tokens appended between
+boundaries, the slot hidden state projected through seeded mirrored weights
+(3072x1024 bf16 ~ N(0, 0.02)) at every boundary, m = 1..512 (final t = 34820).  The
+oracle projects every slot; the slot query and the stored K/V are compared at
+m in {1, 2, 64, 256, 512} (0, 1, 63, 255 and 511 prior slots), the decode at the end.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_kv_attention_amd as M
+import seeded_inputs as SI
+from oracle import masw_oracle as O
+from tests.gpu_driver import np_in
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    M.lib()
+
+
+def _ulp_close(got, ref):
+    ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+    return bool((np.abs(got - ref) <= ulp).all())
+
+
+def test_materialize_chain_3b_to_512_slots():
+    sh = SI.MATERIALIZE_3B
+    S, W, r, B, Hkv, D, hidden = sh.sink, sh.window, sh.interval, sh.batch, sh.n_kv_heads, sh.head_dim, sh.hidden
+    n_chain = SI.MATERIALIZE_CHAIN
+    d = M.Dims(batch=B, n_q_heads=sh.n_q_heads, n_kv_heads=Hkv, head_dim=D, sink=S, window=W, interval=r,
+               max_slots=n_chain, dtype=sh.dtype)
+    layer = M.alloc_layer(d, DEV, fill=float("nan"))
+    layer.n_slots.zero_()
+    seq = M.alloc_seq(B, DEV)
+    ws = M.workspace(d, M.OP_MATERIALIZE, device=DEV)
+    wk, wv = SI.mirrored_weights(sh, 51)
+    wk_d, wv_d = wk.to(DEV), wv.to(DEV)
+    wk_n, wv_n = np_in(wk).astype(np.float64), np_in(wv).astype(np.float64)
+    mems = [O.DraftMemory(S, W, r, Hkv, D, bf16_cache=True) for _ in range(B)]
+    check = {1, 2, 64, 256, 512}
+    t = 0
+    for m in range(1, n_chain + 1):
+        tm = O.boundary_step(m, S, W, r)
+        n = tm - t
+        k, v = SI.token_kv(sh, 51, 0, t + 1, n)
+        t = tm
+        seq.seq_len.fill_(t)
+        M.masw_evict_append(d, layer, seq, k.to(DEV), v.to(DEV))
+        kn, vn = np_in(k), np_in(v)
+        for b, mem in enumerate(mems):
+            mem.append(kn[b], vn[b])
+        h, qg = SI.slot_inputs(sh, 51, 0, m)
+        o = torch.full((B, sh.n_q_heads, D), float("nan"), dtype=sh.dtype, device=DEV)
+        M.masw_materialize_slot(d, layer, seq, h.to(DEV), wk_d, wv_d, qg.to(DEV), o, ws)
+        kg, vg = O.project_slot(np_in(h).astype(np.float64), wk_n, wv_n, Hkv, D, bf16_cache=True)
+        for b, mem in enumerate(mems):
+            assert mem.pending_boundary() == m
+            mem.add_slot(m, kg[b], vg[b])
+        if m in check:
+            qn = np_in(qg).astype(np.float64)
+            ref = np.stack([mem.slot_query(m, qn[b], d.softmax_scale) for b, mem in enumerate(mems)])
+            assert_close(o, ref, torch.bfloat16, f"slot query m={m}")
+            got_k = layer.k_slot[:, :, m - 1].double().cpu().numpy()
+            got_v = layer.v_slot[:, :, m - 1].double().cpu().numpy()
+            assert _ulp_close(got_k, kg) and _ulp_close(got_v, vg), f"slot K/V m={m}"
+            # the slot query saw exactly S + W + (m - 1) keys
+            assert len(O.slot_query_keylist(m, S, W, r)) == S + W + m - 1
+    torch.cuda.synchronize()
+    assert int(seq.err.item()) == 0
+    assert layer.n_slots.cpu().tolist() == [n_chain] * B
+    q = SI.decode_query(sh, 51, 0, t)
+    out = torch.empty((B, sh.n_q_heads, D), dtype=sh.dtype, device=DEV)
+    M.masw_draft_attn(d, layer, seq, q.to(DEV), out, ws)
+    qn = np_in(q).astype(np.float64)
+    ref = np.stack([mem.decode(qn[b], d.softmax_scale) for b, mem in enumerate(mems)])
+    assert_close(out, ref, torch.bfloat16, "decode after the chain")
+
+
+def test_bench_launch_configuration_sampled_rows():
+    """B=8, prefix 32768, the bench's split plan: sampled (sequence, head) rows of the
+    fused append + draft attention against the oracle over the same memory contents."""
+    import bench
+    sh = SI.SWEEP_3B
+    import dataclasses
+    shape = dataclasses.replace(sh, layers=2)
+    t0 = bench.T_HEAD
+    st = bench.Stack(shape, t0 + 64, torch.device(DEV), seed=3, with_full=False)
+    st.set_position(t0)
+    st.seq.seq_len.fill_(t0 + 1)     # the fused step appends position t0 + 1
+    lay = st.layers[1]
+    snap = {n: getattr(lay, n).float().cpu().numpy() for n in ("k_sink", "v_sink", "k_ring", "v_ring", "k_slot", "v_slot")}
+    M.masw_decode_step(st.d, lay, st.seq, st.k_new[1], st.v_new[1], st.q[1], st.out[1], st.ws)
+    torch.cuda.synchronize()
+    assert int(st.seq.err.item()) == 0
+    S, W, r = sh.sink, sh.window, sh.interval
+    t = t0 + 1
+    keys = O.physical_keylist(t, S, W, r)
+    kn, vn = np_in(st.k_new[1]), np_in(st.v_new[1])
+    q = np_in(st.q[1]).astype(np.float64)
+    G = sh.group
+    for b in (0, 3, 7):
+        for kvh in (0, 5):
+            K = np.empty((len(keys), sh.head_dim))
+            V = np.empty_like(K)
+            for j, (seg, row, ident) in enumerate(keys):
+                if seg != 2 and ident == t:          # the new token, from the caller's buffer
+                    K[j], V[j] = kn[b, 0, kvh], vn[b, 0, kvh]
+                else:
+                    name = ("sink", "ring", "slot")[seg]
+                    K[j] = snap["k_" + name][b, kvh, row]
+                    V[j] = snap["v_" + name][b, kvh, row]
+            for g in range(G):
+                h = kvh * G + g
+                ref = O.attend(q[b, h], K, V, st.d.softmax_scale)
+                assert_close(st.out[1][b, h], ref, torch.bfloat16, f"b={b} h={h}")
+    # the new token landed in its ring row
+    c = O.ring_cell(t, S, W, r)
+    assert torch.equal(lay.k_ring[:, :, c], st.k_new[1][:, 0])

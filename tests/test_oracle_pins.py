@@ -424,3 +424,17 @@ def test_verify_matches_torch_masked_sdpa():
     # the last query sees every key, the first sees n_q - 1 fewer
     np.testing.assert_allclose(out[-1], O.fullkv_decode(q[-1], K, V, t, scale), atol=0)
     np.testing.assert_allclose(out[0], O.fullkv_decode(q[0], K, V, t - n_q + 1, scale), atol=0)
+
+
+def test_project_slot_batch_rows_are_independent():
+    rng = np.random.default_rng(12)
+    hidden, Hkv, D = 16, 2, 4
+    wk = rng.normal(size=(hidden, Hkv * D))
+    wv = rng.normal(size=(hidden, Hkv * D))
+    H = rng.normal(size=(3, hidden))
+    kb, vb = O.project_slot(H, wk, wv, Hkv, D, bf16_cache=True)
+    assert kb.shape == (3, Hkv, D)
+    for i in range(3):
+        k1, v1 = O.project_slot(H[i], wk, wv, Hkv, D, bf16_cache=True)
+        np.testing.assert_array_equal(kb[i], k1)
+        np.testing.assert_array_equal(vb[i], v1)

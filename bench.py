@@ -22,9 +22,11 @@ device value is read inside the timed region.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -38,6 +40,9 @@ import draft_kv_attention_amd as M   # noqa: E402
 import seeded_inputs as SI           # noqa: E402
 
 METRIC = "draft attn steps/s + HBM GB/s (% peak) vs prefix 1K-32K, MASW vs full-KV"
+# Counter summary of the dominant kernel (two rocprofv3 --pmc passes of --traffic-probe)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_b8_prefix32768_hbm_traffic.md")
+DECODE_SOURCES = ("decode_attn.hip", "masw_internal.hpp", "masw_device.hpp")
 HBM_PEAK_GBS = 8000.0
 SHAPE = SI.SWEEP_3B
 T_HEAD = 32768
@@ -231,6 +236,28 @@ def graph_per_call_us(fn, calls, replays=5):
     return e0.elapsed_time(e1) * 1e3 / (replays * calls)
 
 
+def decode_source_hash():
+    """sha256 over the sources the decode kernel is built from."""
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "draft_kv_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or
+    None when there is none or the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    src = re.search(r"source_sha256:\s*([0-9a-f]+)", text)
+    tot = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if not src or not tot or src.group(1) != decode_source_hash():
+        return None
+    return int(tot.group(1))
+
+
 def kernel_roofline(stack, t, reps=4):
     """The dominant kernel of the MASW step: the fused append + draft attention launch.
 
@@ -250,7 +277,7 @@ def kernel_roofline(stack, t, reps=4):
     nbytes = stack.attn_bytes(keys_at(t, stack.S, stack.W, stack.r)) + 2 * sh.batch * stack.kv_row_bytes()
     achieved = nbytes / (us * 1e-6) / 1e9
     return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                 kernel="decode_kernel<bf16,128,3> (masw_decode_step)", avg_us=round(us, 2),
                 bytes_per_launch=int(nbytes), prefix=t, launches_timed=L * reps * 5)
 
@@ -367,6 +394,34 @@ def cpu_baseline(budget_s=15.0):
                        f"scaled x{sh.layers * sh.batch} to one 28-layer batch-8 step")
 
 
+def profile_modes(args, dev):
+    """Runs the dominant kernel alone, at the configuration of kernel_roofline."""
+    stack = Stack(SHAPE, T_HEAD + 64, dev, with_full=False)
+    if args.roofline_only:
+        roof = kernel_roofline(stack, T_HEAD)
+        print(json.dumps({"roofline": roof, "source_sha256": decode_source_hash()}), flush=True)
+        return
+    # --traffic-probe: 2 x 28 eager launches of the fused decode step, then a plain
+    # elementwise copy kernel over 256 MiB (torch.mul by 1 into another buffer, 4 launches)
+    # whose FETCH_SIZE / WRITE_SIZE calibrate the counters.
+    stack.set_position(T_HEAD)
+    L = stack.L
+    for i in range(2 * L):
+        M.masw_decode_step(stack.d, stack.layers[i % L], stack.seq, stack.k_new[i % L], stack.v_new[i % L],
+                           stack.q[i % L], stack.out[i % L], stack.ws)
+    torch.cuda.synchronize()
+    copy_bytes = 256 << 20
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    nbytes = stack.attn_bytes(keys_at(T_HEAD, stack.S, stack.W, stack.r)) + 2 * SHAPE.batch * stack.kv_row_bytes()
+    print(json.dumps({"decode_launches": 2 * L, "algorithmic_bytes_per_launch": int(nbytes),
+                      "copy_bytes_per_launch": copy_bytes, "copy_launches": 4,
+                      "source_sha256": decode_source_hash(), "err": int(stack.seq.err.item())}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +430,10 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=48)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the dominant-kernel roofline leg (for rocprofv3 --kernel-trace --stats)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="eager launches of the dominant kernel and a 256 MiB copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the draft path shards by sequence or KV head "
@@ -383,6 +442,9 @@ def main():
     dev = torch.device("cuda:0")
     M.lib()
     sh = SHAPE
+    if args.roofline_only or args.traffic_probe:
+        profile_modes(args, dev)
+        return
     t_max = T_HEAD + args.warmup + args.steps + 8
     if not args.no_sweep:
         t_max = max(t_max, max(SI.SWEEP_PREFIXES) + args.sweep_steps + 40)

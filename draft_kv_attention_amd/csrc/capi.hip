@@ -12,7 +12,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxSplits = 256;   // split partials merged by one work-group
-constexpr long kTargetWorkGroups = 512;   // two per CU on 256 CUs
+constexpr long kCUs = 256;
 constexpr long kMinKeysPerSplit = 128;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -34,12 +34,14 @@ int check_dims(const masw_dims* d, bool masw_memory) {
   return MASW_OK;
 }
 
-// Splits per (sequence, KV head): enough work-groups to cover the chip, but at least
-// ~128 keys each.  The kernels re-derive the chunk from the actual key count.
-int choose_splits(const masw_dims* d, long max_keys) {
+// Splits per (sequence, KV head): enough work-groups to fill every CU once with as many
+// as stay resident together (`per_cu`), but at least ~128 keys each.  The kernels
+// re-derive the chunk from the actual key count.
+int choose_splits(const masw_dims* d, long max_keys, int per_cu = kDecodeResidentPerCU) {
   if (d->num_splits > 0) return d->num_splits;
   const long units = long(d->batch) * d->n_kv_heads;
-  long s = (kTargetWorkGroups + units - 1) / units;
+  const long target = kCUs * per_cu;
+  long s = (target + units - 1) / units;
   s = std::min(s, std::max(1L, (max_keys + kMinKeysPerSplit - 1) / kMinKeysPerSplit));
   return int(std::max(1L, std::min(s, long(kMaxSplits))));
 }
@@ -154,7 +156,10 @@ MASW_API size_t masw_workspace_bytes(const masw_dims* d, int32_t op, int32_t max
   if (op == MASW_OP_FULLKV_DECODE) return plan_workspace(d, choose_splits(d, max_keys), d->n_q_heads).total;
   if (op == MASW_OP_FULLKV_VERIFY) {
     if (n_q < 1) return 0;
-    return plan_workspace(d, choose_splits(d, max_keys), d->n_q_heads * n_q).total;
+    const int rows = d->n_q_heads / d->n_kv_heads * n_q;
+    const bool mfma = d->dtype == MASW_BF16 && d->head_dim == 128 && rows <= 64;
+    const int per_cu = mfma ? verify_resident_per_cu(rows) : kDecodeResidentPerCU;
+    return plan_workspace(d, choose_splits(d, max_keys, per_cu), d->n_q_heads * n_q).total;
   }
   return 0;
 }
@@ -328,12 +333,13 @@ MASW_API int fullkv_verify_attn(const masw_dims* d, const void* k, const void* v
   int st = check_dims(d, false);
   if (st) return st;
   if (!k || !v || !seq_len || !err || !q || !out || max_len < 1 || n_q < 1 || n_q > 16) return MASW_ERR_ARG;
-  const int splits = choose_splits(d, max_len);
   const int rows = d->n_q_heads / d->n_kv_heads * n_q;
+  const bool mfma = d->dtype == MASW_BF16 && d->head_dim == 128 && rows <= 64;
+  const int splits = choose_splits(d, max_len, mfma ? verify_resident_per_cu(rows) : kDecodeResidentPerCU);
   const WsPlan p = plan_workspace(d, splits, d->n_q_heads * n_q);
   if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
   char* base = static_cast<char*>(ws);
-  if (d->dtype == MASW_BF16 && d->head_dim == 128 && rows <= 64) {
+  if (mfma) {
     VerifyArgs a{};
     a.k = k;
     a.v = v;

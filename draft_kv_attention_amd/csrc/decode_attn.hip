@@ -7,9 +7,9 @@
 //
 // Work decomposition (CDNA4, wave64):
 //   grid  = (splits, Hkv, B); each work-group owns one contiguous chunk of the logical
-//           key list of one (sequence, KV head); its 4 waves stride over the chunk in
-//           tiles of kDecodeTileKeys keys, optionally double-buffered (tile i+1 in
-//           flight while tile i is reduced).
+//           key list of one (sequence, KV head); each of its 4 waves streams an equal
+//           contiguous quarter of the chunk in tiles of TK keys (decode_tile_keys), optionally
+//           double-buffered (tile i+1 in flight while tile i is reduced).
 //   wave  = 64/LPR rows of LPR lanes; a row holds one key.  bf16: 8 lanes x 32 bytes
 //           per 256-byte row (D = 128), so a load instruction pair moves 8 whole rows;
 //           q.k partial dots use v_dot2_f32_bf16 and are summed over the 8 lanes with
@@ -58,11 +58,14 @@ __device__ __forceinline__ int decode_keys(const DecodeArgs& a, int t, int have,
   return ks.total();
 }
 
-// Keys per split: ceil(n / splits) rounded up to whole tiles.  A function of (n, splits)
-// only, so two memories with the same key list reduce in the same order.
+// Keys per split: ceil(n / splits) rounded up to a multiple of kSplitRound, so that
+// the waves of a work-group each take an equal contiguous run of whole 8-row groups.
+// A function of (n, splits) only, so two memories with the same key list reduce in
+// the same order.
+constexpr int kSplitRound = 8 * (kDecodeThreads / kWave);
 __device__ __forceinline__ int split_chunk(int n, int n_splits) {
   int c = (n + n_splits - 1) / n_splits;
-  return (c + kDecodeTileKeys - 1) / kDecodeTileKeys * kDecodeTileKeys;
+  return (c + kSplitRound - 1) / kSplitRound * kSplitRound;
 }
 
 // A lane fragment of one row: NW dwords in 16-byte chunks; chunk c sits CH elements
@@ -73,7 +76,8 @@ __device__ __forceinline__ void load_frag(uint32_t (&w)[NW], const T* p) {
   static_assert(NW % 4 == 0, "fragments are whole 16-byte chunks");
 #pragma unroll
   for (int c = 0; c < NW / 4; ++c) {
-    const uint4 x = *reinterpret_cast<const uint4*>(p + c * CH);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p + c * CH);
+    const u32x4_t x = kDecodeNonTemporal ? __builtin_nontemporal_load(src) : *src;
     w[4 * c] = x.x; w[4 * c + 1] = x.y; w[4 * c + 2] = x.z; w[4 * c + 3] = x.w;
   }
 }
@@ -104,13 +108,33 @@ __device__ __forceinline__ float frag_elem(const uint32_t (&w)[NW], int e) {
 }
 
 // Fused append: copy the n_new new tokens of (b, kvh) into sink / ring rows.  An
-// eviction of a token whose block has no slot yet is suppressed and reported.
+// eviction of a token whose block has no slot yet is suppressed and reported.  Packets
+// p < n_new * D / VEC each move 16 bytes of K and of V; when every packet has its own
+// thread, the caller issued the loads at kernel start (pk / pv for packet threadIdx.x)
+// and only the stores are left, so no load round trip sits on the work-group's path.
+// No other work-group of the launch reads these rows: decode reads the new tokens from
+// k_new / v_new, and the ring cells they overwrite hold tokens outside the window.
 template <typename T, int D>
-__device__ void append_rows(const DecodeArgs& a, int b, int kvh, int t, int have, bool report) {
+__device__ __forceinline__ bool append_prefetched(const DecodeArgs& a) {
+  return a.n_new * (D * int(sizeof(T)) / 16) <= kDecodeThreads;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ size_t append_src(const DecodeArgs& a, int b, int kvh, int p) {
+  constexpr int VEC = 16 / int(sizeof(T));
+  constexpr int PKT = D / VEC;
+  const int j = p / PKT;
+  return ((size_t(b) * a.n_new + j) * a.Hkv + kvh) * D + (p - j * PKT) * VEC;
+}
+
+template <typename T, int D>
+__device__ void append_rows(const DecodeArgs& a, int b, int kvh, int t, int have, bool report, u32x4_t pk,
+                            u32x4_t pv) {
   if (t < a.n_new || (a.max_len > 0 && t > a.max_len)) return;   // reported by decode_keys
   constexpr int VEC = 16 / int(sizeof(T));
   constexpr int PKT = D / VEC;
   const size_t unit = size_t(b) * a.Hkv + kvh;
+  const bool pre = append_prefetched<T, D>(a);
   int bits = 0;
   for (int p = threadIdx.x; p < a.n_new * PKT; p += kDecodeThreads) {
     const int j = p / PKT;
@@ -133,51 +157,57 @@ __device__ void append_rows(const DecodeArgs& a, int b, int kvh, int t, int have
       dk = static_cast<T*>(a.wk[1]);
       dv = static_cast<T*>(a.wv[1]);
     }
-    const size_t src = ((size_t(b) * a.n_new + j) * a.Hkv + kvh) * D + d;
-    *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_new) + src);
-    *reinterpret_cast<uint4*>(dv + off) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_new) + src);
+    if (!pre) {
+      const size_t src = append_src<T, D>(a, b, kvh, p);
+      pk = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(a.k_new) + src);
+      pv = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(a.v_new) + src);
+    }
+    *reinterpret_cast<u32x4_t*>(dk + off) = pk;
+    *reinterpret_cast<u32x4_t*>(dv + off) = pv;
   }
   if (bits && report) atomicOr(a.err, bits);
 }
 
-constexpr int kMergeBatch = 16;   // split partials one thread loads at once
-constexpr int kMaxMergeSplits = 256;
+constexpr int kMergeBatch = 8;    // split partials one thread loads at once
 
 // Combine n_valid (max, sum, o) partials of the G query heads of one KV head into out.
+// No LDS and no barrier: every thread loads, for each of its (g, d) outputs, the o
+// values and the (max, sum) pairs of a batch of splits straight into registers (all
+// loads of a batch in flight together) and folds the batch in online, rescaling what it
+// has when the running max grows.  One round trip when n_valid <= kMergeBatch.
 template <typename T, int D, int G>
 __device__ __forceinline__ void merge_partials(const float* part_o, const float* part_ml, size_t row0, int n_splits,
                                                int n_valid, T* outb) {
-  __shared__ float sm_pm[G][kMaxMergeSplits], sm_pl[G][kMaxMergeSplits];
-  __shared__ float sm_M[G];
-  for (int i = threadIdx.x; i < G * n_valid; i += kDecodeThreads) {
-    const int g = i / n_valid, sp = i - (i / n_valid) * n_valid;
-    const float* ml = part_ml + ((row0 + g) * n_splits + sp) * 2;
-    sm_pm[g][sp] = load_partial(ml);
-    sm_pl[g][sp] = load_partial(ml + 1);
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_valid; ++sp) M = fmaxf(M, sm_pm[threadIdx.x][sp]);
-    sm_M[threadIdx.x] = M;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+  constexpr int PER = (G * D + kDecodeThreads - 1) / kDecodeThreads;   // (g, d) outputs per thread
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x + k * kDecodeThreads;
+    if (PER * kDecodeThreads != G * D && idx >= G * D) break;
     const int g = idx / D, d = idx - (idx / D) * D;
     const float* po = part_o + (row0 + g) * n_splits * D + d;
-    const float M = sm_M[g];
-    float L = 0.f, O = 0.f;
+    const float* ml = part_ml + (row0 + g) * n_splits * 2;
+    float M = -INFINITY, L = 0.f, O = 0.f;
     for (int s0 = 0; s0 < n_valid; s0 += kMergeBatch) {
-      float v[kMergeBatch];
+      float pm[kMergeBatch], pl[kMergeBatch], v[kMergeBatch];
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) v[k] = s0 + k < n_valid ? load_partial(&po[size_t(s0 + k) * D]) : 0.f;
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const bool ok = s0 + j < n_valid;
+        pm[j] = ok ? load_partial(&ml[2 * (s0 + j)]) : -INFINITY;
+        pl[j] = ok ? load_partial(&ml[2 * (s0 + j) + 1]) : 0.f;
+        v[j] = ok ? load_partial(&po[size_t(s0 + j) * D]) : 0.f;
+      }
+      float mb = M;
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        if (s0 + k < n_valid) {
-          const float wt = fast_exp2(sm_pm[g][s0 + k] - M);
-          L = fmaf(wt, sm_pl[g][s0 + k], L);
-          O = fmaf(wt, v[k], O);
-        }
+      for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, pm[j]);
+      const float alpha = fast_exp2(M - mb);   // 0 on the first batch (M = -inf)
+      L *= alpha;
+      O *= alpha;
+      M = mb;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const float wt = fast_exp2(pm[j] - M);   // splits past n_valid carry -inf -> 0
+        L = fmaf(wt, pl[j], L);
+        O = fmaf(wt, v[j], O);
       }
     }
     outb[g * D + d] = Elem<T>::from_f32(O / L);
@@ -205,14 +235,12 @@ __device__ __forceinline__ float row_sum(float v) {
 template <int LPR>
 __device__ __forceinline__ float groups_max(float v) {
   if constexpr (LPR == 8) v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false)));
-  v = fmaxf(v, xor_lanes(v, 16));
-  return fmaxf(v, xor_lanes(v, 32));
+  return rows4_max(v);
 }
 template <int LPR>
 __device__ __forceinline__ float groups_sum(float v) {
   if constexpr (LPR == 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
-  v += xor_lanes(v, 16);
-  return v + xor_lanes(v, 32);
+  return rows4_sum(v);
 }
 
 // Where a lane's rows live, as element offsets from the sink base of K (and of V): the
@@ -225,7 +253,22 @@ struct TileSrc {
   int t_old;
 };
 
-// Issue the loads of one tile: row u of this lane is logical key tile + u*RPI + lgrp.
+// Element offsets from kb0 / vb0 of the K and V rows of logical key j.
+struct RowOff {
+  long k, v;
+};
+template <int D>
+__device__ __forceinline__ RowOff row_offsets(int j, const KeySpan& ks, const MemGeom& g, const TileSrc& src) {
+  const KeyRef kr = resolve_key(j, ks, g);
+  const bool is_new = kr.seg != 2 && kr.id > src.t_old;
+  const long row = is_new ? long(kr.id - src.t_old - 1) * src.new_row : long(kr.row) * D;
+  const long dk = is_new ? src.dk_new : (kr.seg == 0 ? 0L : (kr.seg == 1 ? src.dk_ring : src.dk_slot));
+  const long dv = is_new ? src.dv_new : (kr.seg == 0 ? 0L : (kr.seg == 1 ? src.dv_ring : src.dv_slot));
+  return RowOff{dk + row, dv + row};
+}
+
+// Issue the loads of one tile: row u of this lane is logical key tile + u*RPI + lgrp
+// (rows past k1 re-read row k0 and are masked in the reduction).
 template <typename T, int D, int U, int NW, int CH, int RPI>
 __device__ __forceinline__ void load_tile(uint32_t (&fk)[U][NW], uint32_t (&fv)[U][NW], int tile, int k0, int k1,
                                           int lgrp, const KeySpan& ks, const MemGeom& g, const T* kb0,
@@ -233,15 +276,56 @@ __device__ __forceinline__ void load_tile(uint32_t (&fk)[U][NW], uint32_t (&fv)[
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = tile + u * RPI + lgrp;
-    const KeyRef kr = resolve_key(j < k1 ? j : k0, ks, g);
-    const bool is_new = kr.seg != 2 && kr.id > src.t_old;
-    const long row = is_new ? long(kr.id - src.t_old - 1) * src.new_row : long(kr.row) * D;
-    const long dk = is_new ? src.dk_new : (kr.seg == 0 ? 0L : (kr.seg == 1 ? src.dk_ring : src.dk_slot));
-    const long dv = is_new ? src.dv_new : (kr.seg == 0 ? 0L : (kr.seg == 1 ? src.dv_ring : src.dv_slot));
-    load_frag<NW, CH>(fk[u], kb0 + dk + row);
-    load_frag<NW, CH>(fv[u], vb0 + dv + row);
+    const RowOff o = row_offsets<D>(j < k1 ? j : k0, ks, g, src);
+    load_frag<NW, CH>(fk[u], kb0 + o.k);
+    load_frag<NW, CH>(fv[u], vb0 + o.v);
   }
 }
+
+// The same tile as asynchronous copies into one LDS stage of this wave: load
+// instruction i (K rows, then V rows; chunk-major inside a row) writes 64 lanes x 16
+// bytes at stage + i KB, lane l at byte 16 l, so read_tile_lds hands every lane exactly
+// the fragment load_tile would have loaded.  Completion is tracked by vmcnt only.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <typename T, int D, int U, int NW, int CH, int RPI>
+__device__ __forceinline__ void issue_tile_lds(u32x4_t* stage, int tile, int k0, int k1, int lgrp,
+                                               const KeySpan& ks, const MemGeom& g, const T* kb0, const T* vb0,
+                                               const TileSrc src) {
+  constexpr int NC = NW / 4;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = tile + u * RPI + lgrp;
+    const RowOff o = row_offsets<D>(j < k1 ? j : k0, ks, g, src);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb0 + o.k + c * CH),
+                                       (lds_ptr_t)(stage + (u * NC + c) * kWave), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb0 + o.v + c * CH),
+                                       (lds_ptr_t)(stage + ((U + u) * NC + c) * kWave), 16, 0, 0);
+    }
+  }
+}
+
+template <int U, int NW>
+__device__ __forceinline__ void read_tile_lds(uint32_t (&fk)[U][NW], uint32_t (&fv)[U][NW], const u32x4_t* stage,
+                                              int lane) {
+  constexpr int NC = NW / 4;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const u32x4_t x = stage[(u * NC + c) * kWave + lane];
+      const u32x4_t y = stage[((U + u) * NC + c) * kWave + lane];
+      fk[u][4 * c] = x.x; fk[u][4 * c + 1] = x.y; fk[u][4 * c + 2] = x.z; fk[u][4 * c + 3] = x.w;
+      fv[u][4 * c] = y.x; fv[u][4 * c + 1] = y.y; fv[u][4 * c + 2] = y.z; fv[u][4 * c + 3] = y.w;
+    }
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; a field at its maximum does not wait).
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+constexpr int kWaitLgkm0 = 0xf | (0x3 << 14) | (0x7 << 4);
 
 // Online-softmax update of (m, l, acc) with one tile.
 template <typename T, int G, int U, int NW, int EPL, int LPR, int RPI>
@@ -318,14 +402,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   constexpr int NW = EPL * int(sizeof(T)) / 4;   // dwords per lane of one row
   constexpr int VEC = 16 / int(sizeof(T));       // elements per 16-byte chunk
   constexpr int CH = LPR * VEC;                  // elements between a lane's chunks
-  constexpr int U = kDecodeTileKeys / RPI;       // rows per lane per tile
+  constexpr int TK = decode_tile_keys<int(sizeof(T)), D, G>();   // keys per wave tile
+  constexpr int U = TK / RPI;                    // rows per lane per tile
   constexpr int NWAVES = kDecodeThreads / kWave;
-  constexpr int STRIDE = NWAVES * kDecodeTileKeys;
   static_assert(U % 2 == 0, "rows are paired for the bf16 P.V dot products");
+  static_assert(kSplitRound % (NWAVES * RPI) == 0, "a wave's run is whole row groups");
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int lgrp = lane / LPR;
   const int lsub = lane % LPR;
 
@@ -338,11 +423,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 #pragma unroll
   for (int g = 0; g < G; ++g) load_frag<NW, CH>(qw[g], qb + g * D);
 
-  if (a.n_new > 0 && split == 0) append_rows<T, D>(a, b, kvh, t, have, kvh == 0);
+  // Split 0 of every (sequence, KV head) also appends the new tokens: loads now, stores
+  // after its share of the keys.
+  const bool appender = a.n_new > 0 && split == 0;
+  u32x4_t apk = {0, 0, 0, 0}, apv = {0, 0, 0, 0};
+  if (appender && append_prefetched<T, D>(a) && int(threadIdx.x) < a.n_new * (D * int(sizeof(T)) / 16)) {
+    const size_t src = append_src<T, D>(a, b, kvh, threadIdx.x);
+    apk = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(a.k_new) + src);
+    apv = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(a.v_new) + src);
+  }
 
   KeySpan ks;
   const int n = decode_keys(a, t, have, act, ks, split == 0 && kvh == 0 && threadIdx.x == 0);
-  if (n == 0) return;
+  if (n == 0) {
+    if (appender) append_rows<T, D>(a, b, kvh, t, have, kvh == 0, apk, apv);
+    return;
+  }
   const int chunk = split_chunk(n, a.n_splits);
   const int k0 = split * chunk;
   if (k0 >= n) return;
@@ -372,28 +468,62 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 
   const TileSrc src{long(kb1 - kb0), long(kb2 - kb0), long(knb - kb0), long(vb1 - vb0), long(vb2 - vb0),
                      long(vnb - vb0), long(new_row), t_old};
-  if constexpr (kDecodeDoubleBuffer) {
+  // Wave w streams keys [w0, w1) of the chunk, one tile at a time (the last one ragged).
+  const int sub = chunk / NWAVES;
+  const int w0 = k0 + wave * sub;
+  const int w1 = min(w0 + sub, k1);
+  if constexpr (kDecodeLdsPipe) {
+    // kPipeStages tiles of this wave in flight as global->LDS copies; tile i sits in
+    // stage i mod kPipeStages.  Before tile i is read, s_waitcnt leaves only the copies
+    // of the tiles issued after it outstanding (copies complete in issue order); once
+    // its fragments are in registers (lgkmcnt 0) the stage is refilled with tile
+    // i + kPipeStages and tile i is reduced while the copies stream.
+    constexpr int KI = 2 * U * (NW / 4);   // load instructions per tile
+    static_assert(KI == kPipeStageInstr, "a stage holds exactly one tile");
+    __shared__ u32x4_t pipe[NWAVES][kPipeStages][KI * kWave];
+    const int nt = w0 < w1 ? (w1 - w0 + TK - 1) / TK : 0;   // tiles of this wave
+#pragma unroll
+    for (int i = 0; i < kPipeStages; ++i)
+      if (i < nt) issue_tile_lds<T, D, U, NW, CH, RPI>(pipe[wave][i], w0 + i * TK, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
+    uint32_t ka[U][NW], va[U][NW];
+    int st = 0;
+    for (int i = 0; i < nt; ++i) {
+      const int ahead = min(nt - 1 - i, kPipeStages - 1);   // tiles issued after tile i
+      if (kPipeStages == 3 && ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * KI));
+      else if (ahead >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(KI));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      read_tile_lds<U, NW>(ka, va, pipe[wave][st], lane);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      const int tile = w0 + i * TK;
+      if (i + kPipeStages < nt)
+        issue_tile_lds<T, D, U, NW, CH, RPI>(pipe[wave][st], tile + kPipeStages * TK, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
+      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, w1, lgrp, a.scale_log2, qw, m, l, acc);
+      st = st + 1 == kPipeStages ? 0 : st + 1;
+    }
+  } else if constexpr (kDecodeDoubleBuffer) {
     uint32_t ka[U][NW], va[U][NW], kc[U][NW], vc[U][NW];
-    int tile = k0 + wave * kDecodeTileKeys;
-    if (tile < k1) load_tile<T, D, U, NW, CH, RPI>(ka, va, tile, k0, k1, lgrp, ks, a.g, kb0, vb0, src);
-    while (tile < k1) {
-      int nt = tile + STRIDE;
-      if (nt < k1) load_tile<T, D, U, NW, CH, RPI>(kc, vc, nt, k0, k1, lgrp, ks, a.g, kb0, vb0, src);
-      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, k1, lgrp, a.scale_log2, qw, m, l, acc);
+    int tile = w0;
+    if (tile < w1) load_tile<T, D, U, NW, CH, RPI>(ka, va, tile, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
+    while (tile < w1) {
+      int nt = tile + TK;
+      if (nt < w1) load_tile<T, D, U, NW, CH, RPI>(kc, vc, nt, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
+      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, w1, lgrp, a.scale_log2, qw, m, l, acc);
       tile = nt;
-      if (tile >= k1) break;
-      nt = tile + STRIDE;
-      if (nt < k1) load_tile<T, D, U, NW, CH, RPI>(ka, va, nt, k0, k1, lgrp, ks, a.g, kb0, vb0, src);
-      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(kc, vc, tile, k1, lgrp, a.scale_log2, qw, m, l, acc);
+      if (tile >= w1) break;
+      nt = tile + TK;
+      if (nt < w1) load_tile<T, D, U, NW, CH, RPI>(ka, va, nt, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
+      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(kc, vc, tile, w1, lgrp, a.scale_log2, qw, m, l, acc);
       tile = nt;
     }
   } else {
     uint32_t ka[U][NW], va[U][NW];
-    for (int tile = k0 + wave * kDecodeTileKeys; tile < k1; tile += STRIDE) {
-      load_tile<T, D, U, NW, CH, RPI>(ka, va, tile, k0, k1, lgrp, ks, a.g, kb0, vb0, src);
-      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, k1, lgrp, a.scale_log2, qw, m, l, acc);
+    for (int tile = w0; tile < w1; tile += TK) {
+      load_tile<T, D, U, NW, CH, RPI>(ka, va, tile, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
+      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, w1, lgrp, a.scale_log2, qw, m, l, acc);
     }
   }
+
+  if (appender) append_rows<T, D>(a, b, kvh, t, have, kvh == 0, apk, apv);
 
   // Row groups of a wave share the running max; sum their partial l and o.
 #pragma unroll

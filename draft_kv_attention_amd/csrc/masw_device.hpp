@@ -14,6 +14,10 @@ namespace masw {
 
 constexpr int kWave = 64;
 
+// 16 bytes as a native vector (struct types such as uint4 can end up in scratch memory
+// when indexed).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32 (bf16 = upper half of an IEEE binary32)
 // ---------------------------------------------------------------------------
@@ -51,19 +55,27 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float xor_lanes(float v, int mask) {
-  return __shfl_xor(v, mask, kWave);
+// Combine across the four 16-lane rows of a wave on the VALU.  v_permlane16_swap
+// (v_permlane32_swap) with both operands a copy of v returns, in every lane, the values
+// of the lane pair {l, l^16} ({l, l^32}) in a fixed order; no LDS round trip.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-// Combine across the four 16-lane rows of a wave.
-__device__ __forceinline__ float rows4_max(float v) {
-  v = fmaxf(v, xor_lanes(v, 16));
-  return fmaxf(v, xor_lanes(v, 32));
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float rows4_sum(float v) {
-  v += xor_lanes(v, 16);
-  return v + xor_lanes(v, 32);
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float rows4_max(float v) { return max_xor32(max_xor16(v)); }
+__device__ __forceinline__ float rows4_sum(float v) { return sum_xor32(sum_xor16(v)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -9,17 +9,61 @@
 
 namespace masw {
 
-// Keys per wave iteration of the decode kernel, and whether a wave keeps the next
-// tile's loads in flight while it reduces the current one.
+// Decode streaming.  With MASW_DECODE_LDS_PIPE each wave keeps MASW_DECODE_PIPE_STAGES
+// tiles in flight as asynchronous global->LDS copies (global_load_lds_dwordx4) and
+// reduces the oldest one from registers, so the VALU work of one tile overlaps the
+// memory time of the next ones.  Otherwise tiles are loaded straight into registers,
+// optionally double-buffered.  MASW_DECODE_TILE_KEYS (0: per instantiation, see
+// decode_tile_keys) and MASW_DECODE_NT (non-temporal hint) apply to the register path.
+#ifndef MASW_DECODE_LDS_PIPE
+#define MASW_DECODE_LDS_PIPE 1
+#endif
+#ifndef MASW_DECODE_PIPE_STAGES
+#define MASW_DECODE_PIPE_STAGES 2
+#endif
+#ifndef MASW_DECODE_PIPE_STAGE_INSTR
+#define MASW_DECODE_PIPE_STAGE_INSTR 8
+#endif
 #ifndef MASW_DECODE_TILE_KEYS
-#define MASW_DECODE_TILE_KEYS 32
+#define MASW_DECODE_TILE_KEYS 0
 #endif
 #ifndef MASW_DECODE_DOUBLE_BUFFER
 #define MASW_DECODE_DOUBLE_BUFFER 0
 #endif
-constexpr int kDecodeTileKeys = MASW_DECODE_TILE_KEYS;
+#ifndef MASW_DECODE_NT
+#define MASW_DECODE_NT 0
+#endif
+#ifndef MASW_DECODE_THREADS
+#define MASW_DECODE_THREADS 256
+#endif
+constexpr bool kDecodeLdsPipe = MASW_DECODE_LDS_PIPE != 0;
+constexpr int kPipeStages = MASW_DECODE_PIPE_STAGES;
+constexpr int kPipeStageInstr = MASW_DECODE_PIPE_STAGE_INSTR;   // 1 KB load instructions per stage
 constexpr bool kDecodeDoubleBuffer = MASW_DECODE_DOUBLE_BUFFER != 0;
-constexpr int kDecodeThreads = 256;
+constexpr bool kDecodeNonTemporal = MASW_DECODE_NT != 0;
+constexpr int kDecodeThreads = MASW_DECODE_THREADS;
+static_assert(!kDecodeLdsPipe || (kPipeStages >= 2 && kPipeStages <= 3), "two or three stages");
+static_assert(!kDecodeLdsPipe || kPipeStageInstr * (kPipeStages - 1) <= 63, "s_waitcnt vmcnt holds 6 bits");
+// LDS of the pipeline per work-group (it must leave room for the merge buffers).
+constexpr int kPipeLdsBytes = (kDecodeThreads / 64) * kPipeStages * kPipeStageInstr * 1024;
+static_assert(!kDecodeLdsPipe || kPipeLdsBytes <= 128 * 1024, "pipeline LDS fits beside the merge buffers");
+// Decode work-groups per CU that the split heuristic aims for.  Measured on the 3B layer
+// share (B = 8, 8 KV heads, 2.5K keys): one work-group per CU (4 splits) beats two
+// (8 splits) for every loop variant, the extra partials and merge traffic costing more
+// than the extra waves gain.
+constexpr int kDecodeResidentPerCU = 1;
+
+// Keys per wave tile.  Pipeline: one stage holds the K and V rows of a tile,
+// kPipeStageInstr x 64 lanes x 16 bytes.  Register path: as many K/V bytes in flight
+// per wave as fit beside the G query fragments and accumulators without dropping below
+// two waves per SIMD (bf16, D = 128: 64 keys for G <= 3).
+template <int ELEM_BYTES, int D, int G>
+constexpr int decode_tile_keys() {
+  if (kDecodeLdsPipe) return kPipeStageInstr * 1024 / (2 * D * ELEM_BYTES);
+  if (MASW_DECODE_TILE_KEYS > 0) return MASW_DECODE_TILE_KEYS;
+  if (ELEM_BYTES == 2) return G <= 3 || D == 64 ? 64 : 32;
+  return 32;
+}
 
 // Split-K decode attention over one memory (three segments; a full cache is the sink
 // segment alone).  One work-group per (split, KV head, sequence).  With several splits
@@ -109,5 +153,9 @@ struct VerifyArgs {
 };
 
 int launch_verify_mfma(const VerifyArgs& a, hipStream_t s);
+// Verifier work-groups that stay resident per CU for `rows` = G * n_q query rows
+// (measured on 8B / 70B layer shares: 32-row blocks fill the chip best at one per CU,
+// 64-row blocks at two).
+inline int verify_resident_per_cu(int rows) { return rows <= 32 ? 1 : 2; }
 
 }  // namespace masw

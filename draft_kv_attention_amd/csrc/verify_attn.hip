@@ -35,8 +35,6 @@ constexpr int kMaxRows = 64;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-// Native clang vector (not HIP's uint4 struct) so staging arrays stay in registers.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int NB> struct VTile {
   static constexpr int WPR = kVWaves / NB;      // waves per row block

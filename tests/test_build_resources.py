@@ -1,5 +1,5 @@
-"""Every HIP kernel compiles for gfx950 without private (scratch) memory or register
-spills.  A kernel that silently falls back to scratch (an array the compiler could not
+"""Every HIP kernel compiles for gfx950 without private (scratch) memory or VGPR
+spills (an SGPR spill with no scratch is kept in a VGPR lane).  A kernel that silently falls back to scratch (an array the compiler could not
 keep in registers) runs several times slower, so this is checked on the CPU at build
 time from the compiler's own resource report."""
 import concurrent.futures
@@ -41,5 +41,6 @@ def test_no_scratch_no_spills(report):
         for name, res in ks.items():
             kernels += 1
             assert res.get("ScratchSize [bytes/lane]", 0) == 0, (src, name, res)
-            assert res.get("VGPRs Spill", 0) == 0 and res.get("SGPRs Spill", 0) == 0, (src, name, res)
+            # SGPR spills without scratch live in VGPR lanes (v_writelane), no memory.
+            assert res.get("VGPRs Spill", 0) == 0, (src, name, res)
     assert kernels >= 20

@@ -84,8 +84,9 @@ class Stack:
         self.layers, self.wk, self.wv = [], [], []
         for _ in range(self.L):
             lay = M.alloc_layer(self.d, dev, fill=None)
-            lay.k_sink.copy_(rnd(*lay.k_sink.shape)); lay.v_sink.copy_(rnd(*lay.v_sink.shape))
-            lay.k_ring.copy_(rnd(*lay.k_ring.shape)); lay.v_ring.copy_(rnd(*lay.v_ring.shape))
+            kvs = shape.kv_std
+            lay.k_sink.copy_(rnd(*lay.k_sink.shape, std=kvs)); lay.v_sink.copy_(rnd(*lay.v_sink.shape, std=kvs))
+            lay.k_ring.copy_(rnd(*lay.k_ring.shape, std=kvs)); lay.v_ring.copy_(rnd(*lay.v_ring.shape, std=kvs))
             wk, wv = rnd(hid, Hkv * D, std=shape.w_std), rnd(hid, Hkv * D, std=shape.w_std)
             hs = rnd(B * self.max_slots, hid)
             lay.k_slot.copy_((hs @ wk).view(B, self.max_slots, Hkv, D).permute(0, 2, 1, 3))
@@ -95,8 +96,8 @@ class Stack:
             self.wv.append(wv)
         self.seq = M.alloc_seq(B, dev)
         self.ws = M.workspace(self.d, M.OP_MATERIALIZE, device=dev)
-        self.k_new = [rnd(B, 1, Hkv, D) for _ in range(self.L)]
-        self.v_new = [rnd(B, 1, Hkv, D) for _ in range(self.L)]
+        self.k_new = [rnd(B, 1, Hkv, D, std=shape.kv_std) for _ in range(self.L)]
+        self.v_new = [rnd(B, 1, Hkv, D, std=shape.kv_std) for _ in range(self.L)]
         self.q = [rnd(B, Hq, D) for _ in range(self.L)]
         self.out = [torch.empty(B, Hq, D, dtype=shape.dtype, device=dev) for _ in range(self.L)]
         self.h = [rnd(B, hid) for _ in range(self.L)]
@@ -106,8 +107,8 @@ class Stack:
         self.kf, self.vf = [], []
         if with_full:
             for _ in range(self.L):
-                self.kf.append(rnd(B, Hkv, self.full_len, D))
-                self.vf.append(rnd(B, Hkv, self.full_len, D))
+                self.kf.append(rnd(B, Hkv, self.full_len, D, std=shape.kv_std))
+                self.vf.append(rnd(B, Hkv, self.full_len, D, std=shape.kv_std))
             self.fd = M.Dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, dtype=shape.dtype)
             self.seq_full = torch.zeros(B, dtype=torch.int32, device=dev)
             self.err_full = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -123,6 +124,19 @@ class Stack:
         if self.kf:
             self.seq_full.fill_(t)
         self.t = t
+
+    def mirror_full_into_masw(self, t):
+        """Make the MASW memory hold the full cache's own raw rows at position t: sinks
+        1..S and the ring cells of positions t-C+1..t (cell (i-S-1) mod C); slots keep
+        their projected values."""
+        S, C = self.S, self.d.ring
+        lo = max(S + 1, t - C + 1)
+        pos = torch.arange(lo, t + 1, device=self.dev)
+        cells = (pos - S - 1) % C
+        for lay, kf, vf in zip(self.layers, self.kf, self.vf):
+            lay.k_sink.copy_(kf[:, :, :S]); lay.v_sink.copy_(vf[:, :, :S])
+            lay.k_ring[:, :, cells] = kf[:, :, pos - 1]
+            lay.v_ring[:, :, cells] = vf[:, :, pos - 1]
 
     # -- one step ----------------------------------------------------------
     def masw_step(self, boundary):
@@ -193,24 +207,95 @@ class Stack:
         return self.L * (self.attn_bytes(t) + self.shape.batch * self.kv_row_bytes())
 
 
-def time_steps(stack, which, t_start, warmup, steps):
-    """Replay `steps` graph steps from position t_start after `warmup` untimed ones."""
+def time_steps(stack, which, t_start, warmup, steps, quantiles=False):
+    """Replay `steps` graph steps from position t_start after `warmup` untimed ones.
+    Returns (mean ms per step, mean algorithmic bytes per step) and, with quantiles,
+    also (p10, p50, p90) of the per-step durations from an event before every replay."""
     stack.set_position(t_start)
     rep = stack.replay_masw if which == "masw" else stack.replay_full
     for _ in range(warmup):
         rep()
     t0 = stack.t
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
         rep()
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = evs[0].elapsed_time(evs[-1]) / steps
     bytes_fn = stack.masw_step_bytes if which == "masw" else stack.full_step_bytes
     avg_bytes = sum(bytes_fn(t) for t in range(t0 + 1, t0 + steps + 1)) / steps
-    return ms, avg_bytes
+    if not quantiles:
+        return ms, avg_bytes
+    d = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    return ms, avg_bytes, tuple(round(float(np.percentile(d, p)), 4) for p in (10, 50, 90))
+
+
+def linear_fit(xs, ys):
+    """Least-squares ys = a + b xs; returns (a, b, R^2)."""
+    x, y = np.asarray(xs, dtype=np.float64), np.asarray(ys, dtype=np.float64)
+    b, a = np.polyfit(x, y, 1)
+    res = y - (a + b * x)
+    r2 = 1.0 - float(res @ res) / float(((y - y.mean()) ** 2).sum())
+    return float(a), float(b), r2
+
+
+def stream_read_leg(dev, launch_bytes, reps=5):
+    """Measured HBM read rate of a plain streaming kernel (masw_stream_read): over one
+    4 GiB buffer (sustained), and at the decode launch's size, 28 distinct buffers
+    rotated in a HIP graph as the attention layers are."""
+    total = torch.zeros(M.STREAM_SUMS, dtype=torch.int32, device=dev)
+    big = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB
+    big = torch.cat([big, big, big, big])                        # 4 GiB
+    nb = big.numel() * 4
+    M.stream_read(big, total)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        M.stream_read(big, total)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    us_big = float(np.median(ts))
+    del big
+    n16 = launch_bytes // 16 * 16
+    bufs = [torch.ones(n16 // 4, dtype=torch.int32, device=dev) for _ in range(28)]
+    us_small = graph_per_call_us(lambda i: M.stream_read(bufs[i % 28], total), 56)
+    del bufs
+    torch.cuda.empty_cache()
+    return dict(kernel="masw_stream_read (2048 work-groups, 8 x 16 B loads in flight per lane)",
+                sustained_4gib_gbs=round(nb / us_big / 1e3, 1),
+                sustained_pct_peak=round(100 * nb / us_big / 1e3 / HBM_PEAK_GBS, 1),
+                launch_size_bytes=int(n16), launch_size_us=round(us_small, 2),
+                launch_size_gbs=round(n16 / us_small / 1e3, 1),
+                launch_size_pct_peak=round(100 * n16 / us_small / 1e3 / HBM_PEAK_GBS, 1))
+
+
+def single_sequence_leg(dev, steps=64, warmup=10):
+    """BASELINE configuration 1: one sequence at prefix 8192, K,V ~ 0.5 N(0,1), the MASW
+    memory holding the full cache's own raw rows; MASW and full-KV graph steps over the
+    same 28 layers."""
+    sh, t = SI.DRAFT_3B, SI.DRAFT_3B_PREFIX
+    st = Stack(sh, t + steps + warmup + 16, dev, seed=1)
+    st.capture()                   # its eager warm-up steps append into both caches
+    st.mirror_full_into_masw(t)
+    out = dict(workload="masw vs full-KV, 28 layers, batch 1, prefix 8192", prefix=t, batch=1,
+               keys_masw=keys_at(t, sh.sink, sh.window, sh.interval), keys_full=t)
+    for which in ("masw", "full"):
+        ms, nb, q = time_steps(st, which, t, warmup, steps, quantiles=True)
+        out[f"{which}_ms"] = round(ms, 4)
+        out[f"{which}_ms_p10_p50_p90"] = q
+        out[f"{which}_steps_per_s"] = round(1e3 / ms, 2)
+        out[f"{which}_gbs"] = round(nb / (ms * 1e-3) / 1e9, 1)
+        out[f"{which}_pct_peak"] = round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)
+    out["full_over_masw_latency"] = round(out["full_ms"] / out["masw_ms"], 3)
+    out["device_err_bits"] = int(st.seq.err.item()) | int(st.err_full.item())
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
 def graph_per_call_us(fn, calls, replays=5):
@@ -454,7 +539,7 @@ def main():
     print("[bench] graphs captured", file=sys.stderr, flush=True)
 
     # headline: MASW at prefix 32768
-    ms, nbytes = time_steps(stack, "masw", T_HEAD, args.warmup, args.steps)
+    ms, nbytes, head_q = time_steps(stack, "masw", T_HEAD, args.warmup, args.steps, quantiles=True)
     value = 1e3 / ms
     gbs = nbytes / (ms * 1e-3) / 1e9
     print(f"[bench] MASW t={T_HEAD}: {ms:.3f} ms/step {gbs:.0f} GB/s", file=sys.stderr, flush=True)
@@ -473,6 +558,16 @@ def main():
             print(f"[bench] sweep t={t}: masw {row['masw_ms']} ms ({row['masw_gbs']} GB/s), "
                   f"full {row['full_ms']} ms ({row['full_gbs']} GB/s)", file=sys.stderr, flush=True)
 
+    fits = None
+    if sweep:
+        fits = {}
+        for which in ("masw", "full"):
+            a, b, r2 = linear_fit([r[f"keys_{which}"] for r in sweep], [r[f"{which}_ms"] for r in sweep])
+            lat = {r["prefix"]: r[f"{which}_ms"] for r in sweep}
+            fits[which] = dict(a_ms=round(a, 5), b_us_per_key=round(b * 1e3, 6), r2=round(r2, 4),
+                               latency_ratio_32k_over_4k=round(lat[32768] / lat[4096], 3))
+        print(f"[bench] eq.3 fits {fits}", file=sys.stderr, flush=True)
+
     roof = kernel_roofline(stack, T_HEAD)
     print(f"[bench] roofline {roof}", file=sys.stderr, flush=True)
     err_bits = int(stack.seq.err.item()) | int(stack.err_full.item())
@@ -482,6 +577,10 @@ def main():
     torch.cuda.empty_cache()
     ver = verify_leg(dev)
     print(f"[bench] verifier {ver}", file=sys.stderr, flush=True)
+    single = single_sequence_leg(dev)
+    print(f"[bench] batch-1 prefix-8192 {single}", file=sys.stderr, flush=True)
+    sread = stream_read_leg(dev, roof["bytes_per_launch"])
+    print(f"[bench] streaming read {sread}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -498,9 +597,11 @@ def main():
                    "batch": sh.batch, "prefix": T_HEAD, "q_heads": sh.n_q_heads,
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "sink": sh.sink,
                    "window": sh.window, "interval": sh.interval},
+        "ms_per_step_p10_p50_p90": head_q,
         "hbm_gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(value * sh.batch, 1),
-        "fullkv_at_prefix": full_head, "sweep": sweep, "device_err_bits": err_bits,
+        "fullkv_at_prefix": full_head, "sweep": sweep, "eq3_fit": fits, "device_err_bits": err_bits,
+        "batch1_prefix8192": single, "streaming_read": sread,
         "materialization": mat, "verifier": ver,
         "roofline": roof, "cpu_baseline": cpu,
     }

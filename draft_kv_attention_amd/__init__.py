@@ -82,6 +82,7 @@ _SIGS = {
     "masw_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "masw_abi_version": (ctypes.c_int, []),
     "masw_debug_keylist": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P]),
+    "masw_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_int32, _P, _P]),
 }
 
 _lib = None
@@ -381,6 +382,20 @@ def masw_debug_keylist(d: Dims, seq: Seq, back: int = 0, max_keys: Optional[int]
     _ok("masw_debug_keylist", lib().masw_debug_keylist(
         ctypes.byref(dc), ctypes.byref(sc), back, out.data_ptr(), max_keys, _stream(stream)))
     return out
+
+
+STREAM_SUMS = 256   # MASW_STREAM_SUMS
+
+
+def stream_read(buf: torch.Tensor, sums: torch.Tensor, work_groups: int = 0, stream=None) -> None:
+    """Measurement helper: adds every 32-bit word of buf (contiguous, a multiple of 16
+    bytes) modulo 2^32 into sums ([STREAM_SUMS] int32 on the same device, zeroed by the
+    caller); the wrapping total of sums is the wrapping sum of buf's words."""
+    if not buf.is_contiguous() or buf.numel() * buf.element_size() % 16:
+        raise ValueError("buf must be contiguous and a multiple of 16 bytes")
+    _check(sums, "sums", (STREAM_SUMS,), torch.int32)
+    _ok("masw_stream_read", lib().masw_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                                   work_groups, sums.data_ptr(), _stream(stream)))
 
 
 def status_string(st: int) -> str:

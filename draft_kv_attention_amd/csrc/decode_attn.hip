@@ -468,6 +468,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 
   const TileSrc src{long(kb1 - kb0), long(kb2 - kb0), long(knb - kb0), long(vb1 - vb0), long(vb2 - vb0),
                      long(vnb - vb0), long(new_row), t_old};
+  // LDS: the tile stages of the pipeline; once a wave has left its loop its own stages
+  // hold its (g, d) accumulators for the merge of the waves.
+  constexpr int KI = 2 * U * (NW / 4);   // load instructions per tile
+  constexpr int WAVE_O = kDecodeLdsPipe ? kPipeStages * KI * kWave * 4 : G * D;   // floats per wave
+  static_assert(!kDecodeLdsPipe || G * D <= WAVE_O, "a wave's stages hold its accumulators");
+  __shared__ u32x4_t pipe[kDecodeLdsPipe ? NWAVES : 1][kDecodeLdsPipe ? kPipeStages : 1][kDecodeLdsPipe ? KI * kWave : 1];
+  __shared__ float sm_o_regs[kDecodeLdsPipe ? 1 : NWAVES * G * D];
+  float* const sm_o = kDecodeLdsPipe ? reinterpret_cast<float*>(&pipe[0][0][0]) : sm_o_regs;
+
   // Wave w streams keys [w0, w1) of the chunk, one tile at a time (the last one ragged).
   const int sub = chunk / NWAVES;
   const int w0 = k0 + wave * sub;
@@ -478,9 +487,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     // of the tiles issued after it outstanding (copies complete in issue order); once
     // its fragments are in registers (lgkmcnt 0) the stage is refilled with tile
     // i + kPipeStages and tile i is reduced while the copies stream.
-    constexpr int KI = 2 * U * (NW / 4);   // load instructions per tile
     static_assert(KI == kPipeStageInstr, "a stage holds exactly one tile");
-    __shared__ u32x4_t pipe[NWAVES][kPipeStages][KI * kWave];
     const int nt = w0 < w1 ? (w1 - w0 + TK - 1) / TK : 0;   // tiles of this wave
 #pragma unroll
     for (int i = 0; i < kPipeStages; ++i)
@@ -534,7 +541,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   }
 
   __shared__ float sm_m[NWAVES][G], sm_l[NWAVES][G];
-  __shared__ float sm_o[NWAVES][G][D];
   __shared__ int sm_last;
   if (lane == 0) {
 #pragma unroll
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave][g][(e / VEC) * CH + lsub * VEC + e % VEC] = acc[g][e];
+      for (int e = 0; e < EPL; ++e) sm_o[wave * WAVE_O + g * D + (e / VEC) * CH + lsub * VEC + e % VEC] = acc[g][e];
   }
   __syncthreads();
 
@@ -560,7 +566,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     for (int w = 0; w < NWAVES; ++w) {
       const float wt = fast_exp2(sm_m[w][g] - M);   // idle waves carry m = -inf -> 0
       L = fmaf(wt, sm_l[w][g], L);
-      O = fmaf(wt, sm_o[w][g][d], O);
+      O = fmaf(wt, sm_o[w * WAVE_O + g * D + d], O);
     }
     if (n_valid == 1) {
       outb[g * D + d] = Elem<T>::from_f32(O / L);

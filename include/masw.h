@@ -231,6 +231,17 @@ MASW_API int masw_abi_version(void);
 MASW_API int masw_debug_keylist(const masw_dims* dims, const masw_seq* seq, int32_t back,
                                 int32_t* out, int32_t max_keys, hipStream_t stream);
 
+/* Measurement helper, not part of the method: a plain streaming read of
+ * p[0..bytes) that adds every 32-bit word modulo 2^32 into the MASW_STREAM_SUMS
+ * counters sums[] (device, caller-zeroed; calls accumulate): the wrapping total of
+ * sums[] is the wrapping sum of the words.  Reports the HBM read rate a simple kernel
+ * reaches on this device, the measured reference for the attention kernels' GB/s.
+ * bytes must be a positive multiple of 16 and p 16-byte aligned (else MASW_ERR_ARG);
+ * work_groups <= 0 picks 2048 contiguous chunks. */
+#define MASW_STREAM_SUMS 256
+MASW_API int masw_stream_read(const void* p, size_t bytes, int32_t work_groups, uint32_t* sums,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -79,6 +79,14 @@ def test_null_arguments_rejected_on_host(lib):
                                      1, 1, 1, 1, 1, 0, 1 << 20, 1 << 30, None) == -3
 
 
+def test_stream_read_rejects_bad_sizes_on_host(lib):
+    assert lib.masw_stream_read(None, 16, 0, 1 << 20, None) == -1
+    assert lib.masw_stream_read(1 << 20, 0, 0, 1 << 20, None) == -1
+    assert lib.masw_stream_read(1 << 20, 24, 0, 1 << 20, None) == -1
+    assert lib.masw_stream_read((1 << 20) + 4, 32, 0, 1 << 20, None) == -1
+    assert lib.masw_stream_read(1 << 20, 32, -1, 1 << 20, None) == -1
+
+
 def test_workspace_sizes(lib):
     d = _dims(batch=8)
     a = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_DRAFT_ATTN, 0, 0)

@@ -49,11 +49,12 @@ int choose_splits(const masw_dims* d, long max_keys, int per_cu = kDecodeResiden
 long masw_max_keys(const masw_dims* d) { return long(d->sink) + d->window + d->max_slots + 1; }
 
 struct WsPlan {
-  size_t flags, counters, part_o, part_ml, total;
+  size_t flags, counters, part_o, part_ml, proj_counters, proj_part, total;
 };
 
 // [per-sequence flags][per-(sequence, KV head) split tickets][partial o][partial max/sum]
-WsPlan plan_workspace(const masw_dims* d, int splits, int rows_per_seq) {
+// and, for materialization, [projection tickets][projection partial sums].
+WsPlan plan_workspace(const masw_dims* d, int splits, int rows_per_seq, bool projection = false) {
   WsPlan p;
   const size_t rows = size_t(d->batch) * rows_per_seq;
   p.flags = 0;
@@ -62,7 +63,12 @@ WsPlan plan_workspace(const masw_dims* d, int splits, int rows_per_seq) {
   const size_t po = splits > 1 ? rows * splits * d->head_dim * sizeof(float) : 0;
   p.part_ml = p.part_o + align_up(po);
   const size_t pml = splits > 1 ? rows * splits * 2 * sizeof(float) : 0;
-  p.total = p.part_ml + align_up(pml);
+  p.proj_counters = p.part_ml + align_up(pml);
+  const size_t groups = (size_t(d->batch) + 15) / 16, N = size_t(d->n_kv_heads) * d->head_dim;
+  const size_t pc = projection ? groups * 2 * (N / 64) * sizeof(int32_t) : 0;
+  p.proj_part = p.proj_counters + align_up(pc);
+  const size_t pp = projection ? groups * 2 * kMaxProjectSplits * 16 * N * sizeof(float) : 0;
+  p.total = p.proj_part + align_up(pp);
   return p;
 }
 
@@ -150,7 +156,7 @@ MASW_API size_t masw_workspace_bytes(const masw_dims* d, int32_t op, int32_t max
   if (check_dims(d, masw_op) != MASW_OK) return 0;
   if (masw_op) {
     const int splits = choose_splits(d, masw_max_keys(d));
-    return plan_workspace(d, splits, d->n_q_heads).total;
+    return plan_workspace(d, splits, d->n_q_heads, op == MASW_OP_MATERIALIZE).total;
   }
   if (max_keys < 1) return 0;
   if (op == MASW_OP_FULLKV_DECODE) return plan_workspace(d, choose_splits(d, max_keys), d->n_q_heads).total;
@@ -292,9 +298,10 @@ MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, cons
     return MASW_ERR_ARG;
   if (d->dtype == MASW_BF16 && hidden % 8) return MASW_ERR_SHAPE;
   const int splits = choose_splits(d, masw_max_keys(d));
-  const WsPlan p = plan_workspace(d, splits, d->n_q_heads);
+  const WsPlan p = plan_workspace(d, splits, d->n_q_heads, true);
   if ((st = check_ws(ws, ws_bytes, p.total))) return st;
-  int32_t* active = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.flags);
+  char* base = static_cast<char*>(ws);
+  int32_t* active = reinterpret_cast<int32_t*>(base + p.flags);
 
   ProjectArgs pa{};
   pa.h = h;
@@ -311,6 +318,10 @@ MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, cons
   pa.Hkv = d->n_kv_heads;
   pa.D = d->head_dim;
   pa.hidden = hidden;
+  pa.k_per_split = project_k_per_split(hidden);
+  pa.ksplits = project_splits(hidden);
+  pa.counters = reinterpret_cast<int32_t*>(base + p.proj_counters);
+  pa.part = reinterpret_cast<float*>(base + p.proj_part);
   if ((st = launch_project(pa, d->dtype, stream))) return st;
 
   DecodeArgs a{};

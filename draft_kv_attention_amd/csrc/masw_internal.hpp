@@ -132,7 +132,25 @@ struct ProjectArgs {
   int32_t* active;          // [B] workspace
   MemGeom g;
   int B, Hkv, D, hidden;
+  // bf16: the hidden dimension is cut into ksplits slices of k_per_split rows (a
+  // multiple of 128); with ksplits > 1 the slices' partial sums go through part
+  // ([groups of 16 sequences][2][ksplits][16][Hkv*D] fp32) and the per-column-block
+  // tickets counters ([groups][2][Hkv*D/64], zero between calls).
+  int ksplits, k_per_split;
+  float* part;
+  int32_t* counters;
 };
+
+constexpr int kMaxProjectSplits = 8;
+// Hidden rows per projection slice and the number of slices for a given hidden size.
+inline int project_k_per_split(int hidden) {
+  const int per = (hidden + kMaxProjectSplits - 1) / kMaxProjectSplits;
+  return (per + 127) / 128 * 128;
+}
+inline int project_splits(int hidden) {
+  const int per = project_k_per_split(hidden);
+  return (hidden + per - 1) / per;
+}
 
 int launch_project(const ProjectArgs& a, int dtype, hipStream_t s);
 

@@ -3,12 +3,9 @@
 // (head k = columns k*D .. k*D+D-1), plus the per-sequence boundary decision that
 // gates the slot query launched after it.
 //
-// bf16: a dense contraction on the matrix cores.  Each work-group owns 64 output
-// columns of one matrix and all hidden rows; its 16 waves split the hidden dimension.
-// Per 32-row step a wave loads a [32 k][64 n] weight tile with fully coalesced 16-byte
-// loads, writes it transposed into its own LDS tile, and feeds four
-// v_mfma_f32_16x16x32_bf16 (A = H rows, zero-padded to 16; B = the transposed tile).
-// The 16 wave partials are summed in LDS in a fixed order (deterministic).
+// bf16: a dense contraction on the matrix cores, spread over 64-column blocks, the two
+// matrices and up to kMaxProjectSplits slices of the hidden dimension (256 work-groups
+// at the 3B shape); see project_mfma_kernel.
 // fp32 caches (small models) use a plain per-column VALU loop.
 #include "masw_internal.hpp"
 
@@ -29,37 +26,55 @@ __device__ __forceinline__ int boundary_slot(const ProjectArgs& a, int b, int& b
   return m;
 }
 
-constexpr int kCols = 64;        // output columns per work-group
-constexpr int kWaves = 16;
-constexpr int kStepK = 32;       // hidden rows per MFMA step
+constexpr int kCols = 64;          // output columns per work-group
+constexpr int kPWaves = 4;
+constexpr int kStepK = 32;         // hidden rows per MFMA step
+constexpr int kPF = 4;             // steps whose weight loads a wave keeps in flight together
 constexpr int kTRow = kStepK + 8;  // transposed tile row (bf16), padded: 80 bytes
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t u16_of(const uint4& v, int e) {
+__device__ __forceinline__ uint32_t u16_of(const u32x4_t& v, int e) {
   const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-__global__ __launch_bounds__(kWaves * kWave) void project_mfma_kernel(const ProjectArgs a) {
-  const int nblk = blockIdx.x, which = blockIdx.y, z = blockIdx.z;
+// Orders this wave's LDS accesses around a tile hand-over between its lanes (LDS
+// executes one wave's instructions in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// grid = (N / 64 column blocks, 2 matrices, ksplits x groups of 16 sequences).  A
+// work-group reduces hidden rows [ks * k_per_split, +k_per_split) of its 64 columns;
+// each of its 4 waves takes a contiguous quarter, keeps kPF steps of weight loads in
+// flight, transposes each [32 k][64 n] tile through its own LDS tile and feeds four
+// v_mfma_f32_16x16x32_bf16 (A = H rows, zero-padded to 16; B = the transposed tile).
+// Waves are summed in LDS in a fixed order; with several hidden splits the
+// last-arriving work-group of the column block adds the split partials in split order
+// (the ticket protocol of the decode merge), so the result is deterministic.
+__global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const ProjectArgs a) {
+  const int nblk = blockIdx.x, which = blockIdx.y;
+  const int bg = blockIdx.z / a.ksplits, ks = blockIdx.z - (blockIdx.z / a.ksplits) * a.ksplits;
   const int N = a.Hkv * a.D;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
   __shared__ int sm_m[16];
-  __shared__ int sm_any;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * kCols * kTRow];
+  __shared__ int sm_any, sm_last;
+  __shared__ __attribute__((aligned(16))) float red[kPWaves * 16 * kCols];
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[kPWaves * kCols * kTRow];
 
   if (tid == 0) sm_any = 0;
   __syncthreads();
   if (tid < 16) {
-    const int b = z * 16 + tid;
+    const int b = bg * 16 + tid;
     int bits = 0, m = 0;
     if (b < a.B) m = boundary_slot(a, b, bits);
     sm_m[tid] = m;
     if (m) atomicOr(&sm_any, 1);
-    if (nblk == 0 && which == 0 && b < a.B) {
+    if (nblk == 0 && which == 0 && ks == 0 && b < a.B) {
       a.active[b] = m;
       if (bits) atomicOr(a.err, bits);
     }
@@ -69,65 +84,110 @@ __global__ __launch_bounds__(kWaves * kWave) void project_mfma_kernel(const Proj
 
   const uint16_t* Wm = static_cast<const uint16_t*>(which ? a.w_v : a.w_k);
   const uint16_t* H = static_cast<const uint16_t*>(a.h);
-  uint16_t* wt = smem + wave * kCols * kTRow;
-  const int iters = (a.hidden + kWaves * kStepK - 1) / (kWaves * kStepK);
-  const int brow = z * 16 + (lane & 15);
+  uint16_t* wt = tiles + wave * kCols * kTRow;   // this wave's transposed tile
+  const int k_wave = a.k_per_split / kPWaves;                 // hidden rows of this wave
+  const int kw0 = ks * a.k_per_split + wave * k_wave;
+  const int n_steps = k_wave / kStepK;
+  const int brow = bg * 16 + (lane & 15);
   const int col8 = lane & 7, kq = lane >> 3;   // loader: 8 lanes per 128-byte row segment
 
   f32x4_t acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = 0; it < iters; ++it) {
-    const int kk = (wave * iters + it) * kStepK;
-    uint4 wv[4];
+  for (int s0 = 0; s0 < n_steps; s0 += kPF) {
+    u32x4_t wv[kPF][4];
+    u32x4_t av[kPF];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = kk + 4 * kq + i;
-      wv[i] = k < a.hidden
-                  ? *reinterpret_cast<const uint4*>(Wm + size_t(k) * N + nblk * kCols + col8 * 8)
-                  : make_uint4(0, 0, 0, 0);
-    }
-    // transposed store: tile row n holds 32 consecutive k of column n
+    for (int p = 0; p < kPF; ++p) {
+      const int kk = kw0 + (s0 + p) * kStepK;
+      const bool on = s0 + p < n_steps;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 x;
-      x.x = u16_of(wv[0], e) | (u16_of(wv[1], e) << 16);
-      x.y = u16_of(wv[2], e) | (u16_of(wv[3], e) << 16);
-      *reinterpret_cast<uint2*>(wt + (col8 * 8 + e) * kTRow + 4 * kq) = x;
+      for (int i = 0; i < 4; ++i) {
+        const int k = kk + 4 * kq + i;
+        wv[p][i] = on && k < a.hidden
+                       ? *reinterpret_cast<const u32x4_t*>(Wm + size_t(k) * N + nblk * kCols + col8 * 8)
+                       : u32x4_t{0, 0, 0, 0};
+      }
+      const int ka = kk + (lane >> 4) * 8;
+      av[p] = on && brow < a.B && ka < a.hidden
+                  ? *reinterpret_cast<const u32x4_t*>(H + size_t(brow) * a.hidden + ka)
+                  : u32x4_t{0, 0, 0, 0};
     }
-    uint4 av = make_uint4(0, 0, 0, 0);
-    const int ka = kk + (lane >> 4) * 8;
-    if (brow < a.B && ka < a.hidden) av = *reinterpret_cast<const uint4*>(H + size_t(brow) * a.hidden + ka);
-    __syncthreads();
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const uint4 bv = *reinterpret_cast<const uint4*>(wt + (nt * 16 + (lane & 15)) * kTRow + (lane >> 4) * 8);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                        __builtin_bit_cast(bf16x8_t, bv), acc[nt], 0, 0, 0);
+    for (int p = 0; p < kPF; ++p) {
+      if (s0 + p >= n_steps) break;
+      // transposed store: tile row n holds 32 consecutive k of column n
+      wave_lds_sync();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t x0 = u16_of(wv[p][0], e) | (u16_of(wv[p][1], e) << 16);
+        uint32_t x1 = u16_of(wv[p][2], e) | (u16_of(wv[p][3], e) << 16);
+        *reinterpret_cast<uint2*>(wt + (col8 * 8 + e) * kTRow + 4 * kq) = make_uint2(x0, x1);
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(wt + (nt * 16 + (lane & 15)) * kTRow + (lane >> 4) * 8);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[p]),
+                                                          __builtin_bit_cast(bf16x8_t, bv), acc[nt], 0, 0, 0);
+      }
     }
-    __syncthreads();
   }
 
   // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16)+i of column lane%16.
-  float* red = reinterpret_cast<float*>(smem);   // [waves][16 rows][64 cols]
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       red[(wave * 16 + (lane >> 4) * 4 + i) * kCols + nt * 16 + (lane & 15)] = acc[nt][i];
   __syncthreads();
-  const int row = tid / kCols, col = tid % kCols;
-  float s = 0.f;
+  constexpr int kOut = 16 * kCols / (kPWaves * kWave);   // outputs per thread
+  float s[kOut];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += red[(w * 16 + row) * kCols + col];
-  const int b = z * 16 + row;
-  const int m = sm_m[row];
-  if (b < a.B && m > 0) {
-    const int n = nblk * kCols + col;
-    const int kvh = n / a.D, d = n - (n / a.D) * a.D;
-    uint16_t* dst = static_cast<uint16_t*>(which ? a.v_slot : a.k_slot);
-    dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = f32_to_bf16(s);
+  for (int j = 0; j < kOut; ++j) {
+    const int idx = tid + j * kPWaves * kWave;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPWaves; ++w) v += red[w * 16 * kCols + idx];
+    s[j] = v;
+  }
+  uint16_t* dst = static_cast<uint16_t*>(which ? a.v_slot : a.k_slot);
+  if (a.ksplits > 1) {
+    // publish this split's partial; the last split of the column block adds them up
+    float* part = a.part + (size_t(bg * 2 + which) * a.ksplits) * 16 * N;
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int idx = tid + j * kPWaves * kWave;
+      store_partial(&part[size_t(ks) * 16 * N + (idx / kCols) * N + nblk * kCols + idx % kCols], s[j]);
+    }
+    int32_t* cnt = a.counters + (bg * 2 + which) * (N / kCols) + nblk;
+    if (!split_arrive(cnt, a.ksplits, &sm_last)) return;
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int idx = tid + j * kPWaves * kWave;
+      const float* pp = part + (idx / kCols) * N + nblk * kCols + idx % kCols;
+      float v[kMaxProjectSplits];
+#pragma unroll
+      for (int q = 0; q < kMaxProjectSplits; ++q) v[q] = q < a.ksplits ? load_partial(&pp[size_t(q) * 16 * N]) : 0.f;
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxProjectSplits; ++q) t += v[q];   // split order; absent splits add 0
+      s[j] = t;
+    }
+    if (tid == 0) reset_ticket(cnt);
+  }
+#pragma unroll
+  for (int j = 0; j < kOut; ++j) {
+    const int idx = tid + j * kPWaves * kWave;
+    const int row = idx / kCols, col = idx % kCols;
+    const int b = bg * 16 + row;
+    const int m = sm_m[row];
+    if (b < a.B && m > 0) {
+      const int n = nblk * kCols + col;
+      const int kvh = n / a.D, d = n - (n / a.D) * a.D;
+      dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = f32_to_bf16(s[j]);
+    }
   }
 }
 
@@ -159,7 +219,9 @@ __global__ __launch_bounds__(256) void project_valu_kernel(const ProjectArgs a) 
 int launch_project(const ProjectArgs& a, int dtype, hipStream_t s) {
   const int N = a.Hkv * a.D;
   if (dtype == MASW_BF16) {
-    hipLaunchKernelGGL(project_mfma_kernel, dim3(N / kCols, 2, (a.B + 15) / 16), dim3(kWaves * kWave), 0, s, a);
+    if (a.ksplits < 1 || a.ksplits > kMaxProjectSplits || a.k_per_split % (kPWaves * kStepK)) return MASW_ERR_ARG;
+    hipLaunchKernelGGL(project_mfma_kernel, dim3(N / kCols, 2, a.ksplits * ((a.B + 15) / 16)),
+                       dim3(kPWaves * kWave), 0, s, a);
   } else {
     hipLaunchKernelGGL(project_valu_kernel<float>, dim3((2 * N + 255) / 256, a.B), dim3(256), 0, s, a);
   }

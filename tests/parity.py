@@ -51,3 +51,17 @@ def assert_close(gpu, ref, dtype, what=""):
     s = compare(gpu, ref, dtype)
     assert close(gpu, ref, dtype), f"{what}: {s} vs tolerance {TOL[dtype]}"
     return s
+
+
+def slot_bound(h, w, n_kv_heads, head_dim):
+    """Per-element allowance for a stored slot K/V (the bf16 rounding of an fp32 sum
+    H W_g): the forward error bound of an fp32 dot product of length n in any summation
+    order, n * 2^-24 * sum_k |h_k w_k|, shaped [..., Hkv, D].  It is added to one bf16 ulp
+    of the oracle's rounded fp64 value; it matters only where the sum cancels."""
+    h, w = np.abs(np.asarray(h, np.float64)), np.abs(np.asarray(w, np.float64))
+    return (h.shape[-1] * 2.0 ** -24 * (h @ w)).reshape(h.shape[:-1] + (n_kv_heads, head_dim))
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 values at |x| (8 significant bits)."""
+    return np.ldexp(1.0, np.frexp(np.abs(np.asarray(x, np.float64)))[1] - 8)

@@ -93,7 +93,7 @@ def test_workspace_sizes(lib):
     b = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_MATERIALIZE, 0, 0)
     f = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_FULLKV_DECODE, 32768, 0)
     v = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_FULLKV_VERIFY, 32774, 6)
-    assert a > 0 and b == a and f > 0 and v > 0
+    assert a > 0 and b > a and f > 0 and v > 0   # materialization adds the projection partials
     assert lib.masw_workspace_bytes(ctypes.byref(d), M.OP_FULLKV_DECODE, 0, 0) == 0
     assert all(x % 256 == 0 for x in (a, b, f, v))
 

@@ -16,7 +16,7 @@ import draft_kv_attention_amd as M
 import seeded_inputs as SI
 from oracle import masw_oracle as O
 from tests.gpu_driver import LayerDriver, np_in, shape_of
-from tests.parity import assert_close
+from tests.parity import assert_close, bf16_ulp, slot_bound
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -168,14 +168,17 @@ def test_3b_layer_bf16_to_8192():
     assert slot_seen == [1, 2, 3, 50, 95]
     assert drv.err() == 0
     assert drv.layer.n_slots.cpu().tolist() == [95, 95]
-    # stored slot K/V are the bf16 rounding of H W_g: within one bf16 ulp of the oracle's
-    for which, buf in ((0, drv.layer.k_slot), (1, drv.layer.v_slot)):
+    # stored slot K/V are the bf16 rounding of H W_g: within one bf16 ulp of the oracle's,
+    # widened by the fp32 dot-product error bound where the sum cancels
+    S, W, r = drv.shape.sink, drv.shape.window, drv.shape.interval
+    for which, buf, w in ((0, drv.layer.k_slot, drv.wk_np), (1, drv.layer.v_slot, drv.wv_np)):
         got = buf.double().cpu().numpy()
         for b, mem in enumerate(drv.mems):
             for m in (1, 50, 95):
                 ref = mem.slots[m][which]
-                ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
-                assert (np.abs(got[b, :, m - 1] - ref) <= ulp).all()
+                h = np_in(SI.slot_inputs(drv.shape, drv.seed, 0, O.boundary_step(m, S, W, r))[0][b])
+                allow = bf16_ulp(ref) + slot_bound(h.astype(np.float64), w, ref.shape[0], ref.shape[1])
+                assert (np.abs(got[b, :, m - 1] - ref) <= allow).all()
 
 
 # ---------------------------------------------------------------------------

@@ -346,7 +346,8 @@ MASW_API int fullkv_verify_attn(const masw_dims* d, const void* k, const void* v
   if (!k || !v || !seq_len || !err || !q || !out || max_len < 1 || n_q < 1 || n_q > 16) return MASW_ERR_ARG;
   const int rows = d->n_q_heads / d->n_kv_heads * n_q;
   const bool mfma = d->dtype == MASW_BF16 && d->head_dim == 128 && rows <= 64;
-  const int splits = choose_splits(d, max_len, mfma ? verify_resident_per_cu(rows) : kDecodeResidentPerCU);
+  int splits = choose_splits(d, max_len, mfma ? verify_resident_per_cu(rows) : kDecodeResidentPerCU);
+  if (mfma) splits = std::min(splits, kMaxVerifySplits);   // its merge keeps [rows][splits] weights in LDS
   const WsPlan p = plan_workspace(d, splits, d->n_q_heads * n_q);
   if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
   char* base = static_cast<char*>(ws);

@@ -74,54 +74,87 @@ __device__ __forceinline__ void stage_tile(const u32x4_t (&kr)[PT], const u32x4_
   }
 }
 
-// Combine n_valid (max, sum, o) partials of the R rows of one KV head into out.  All
-// loads of a batch of splits are issued before any is used.
-__device__ __forceinline__ void merge_verify_partials(const VerifyArgs& a, int b, int kvh, int R, int n_valid) {
-  constexpr int kBatch = 16;
-  __shared__ float sm_M[kMaxRows];
+// Partial / output row of query row `row` (= g * n_q + j) of KV head kvh.
+__device__ __forceinline__ size_t verify_prow(const VerifyArgs& a, int b, int kvh, int row) {
   const int G = a.Hq / a.Hkv;
+  const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
+  return (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
+}
+
+// Combine n_valid (max, sum, o) partials of the R rows of one KV head into out.
+// Phase 1: one thread per row loads every split's (max, sum) and leaves the normalized
+// split weights exp2(m_s - M) / L in sm_w ([R][n_valid] floats of LDS the caller no
+// longer needs).  Phase 2: thread t owns column d = t % 128 of the rows t / 128,
+// t / 128 + 2, ...; it issues the o loads of kRowBatch rows x kSplitBatch splits
+// together and accumulates in registers, so the merge costs a few round trips.
+static_assert(kMaxVerifySplits * kMaxRows * 4 <= 32 * 1024, "split weights fit in the tile buffers");
+__device__ __forceinline__ void merge_verify_partials(const VerifyArgs& a, int b, int kvh, int R, int n_valid,
+                                                      float* sm_w) {
+  constexpr int kRowBatch = 8;
+  constexpr int kSplitBatch = 8;
   uint16_t* out = static_cast<uint16_t*>(a.out);
   if (threadIdx.x < R) {
-    const int row = threadIdx.x;
-    const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
-    const size_t prow = (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
-    const float* ml = a.part_ml + prow * a.n_splits * 2;
+    const float* ml = a.part_ml + verify_prow(a, b, kvh, threadIdx.x) * a.n_splits * 2;
+    float* w_row = sm_w + threadIdx.x * n_valid;
     float M = -INFINITY;
-    for (int s0 = 0; s0 < n_valid; s0 += kBatch) {
-      float mm[kBatch];
+    for (int s0 = 0; s0 < n_valid; s0 += kSplitBatch) {
+      float mm[kSplitBatch];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) mm[k] = s0 + k < n_valid ? load_partial(&ml[2 * (s0 + k)]) : -INFINITY;
+      for (int k = 0; k < kSplitBatch; ++k) mm[k] = s0 + k < n_valid ? load_partial(&ml[2 * (s0 + k)]) : -INFINITY;
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mm[k]);
+      for (int k = 0; k < kSplitBatch; ++k) M = fmaxf(M, mm[k]);
     }
-    sm_M[row] = M;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < R * kD; idx += kVThreads) {
-    const int row = idx / kD, d = idx - (idx / kD) * kD;
-    const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
-    const size_t prow = (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
-    const float* ml = a.part_ml + prow * a.n_splits * 2;
-    const float* po = a.part_o + prow * a.n_splits * kD + d;
-    const float M = sm_M[row];
-    float L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < n_valid; s0 += kBatch) {
-      float v[kBatch], mm[kBatch], ll[kBatch];
+    const float Mr = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    for (int s0 = 0; s0 < n_valid; s0 += kSplitBatch) {
+      float mm[kSplitBatch], ll[kSplitBatch];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
+      for (int k = 0; k < kSplitBatch; ++k) {
         const bool in = s0 + k < n_valid;
-        v[k] = in ? load_partial(&po[size_t(s0 + k) * kD]) : 0.f;
         mm[k] = in ? load_partial(&ml[2 * (s0 + k)]) : -INFINITY;
         ll[k] = in ? load_partial(&ml[2 * (s0 + k) + 1]) : 0.f;
       }
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const float w = fast_exp2(mm[k] - M);   // splits past a row's causal limit carry -inf
+      for (int k = 0; k < kSplitBatch; ++k) {
+        const float w = fast_exp2(mm[k] - Mr);   // splits past a row's causal limit carry -inf
         L = fmaf(w, ll[k], L);
-        O = fmaf(w, v[k], O);
+        if (s0 + k < n_valid) w_row[s0 + k] = w;
       }
     }
-    out[prow * kD + d] = f32_to_bf16(O / L);
+    const float inv = 1.f / L;
+    for (int sp = 0; sp < n_valid; ++sp) w_row[sp] *= inv;
+  }
+  __syncthreads();
+  const int d = threadIdx.x % kD, r0 = threadIdx.x / kD;
+  constexpr int kRowStep = kVThreads / kD;
+  for (int rb = r0; rb < R; rb += kRowStep * kRowBatch) {
+    float O[kRowBatch];
+#pragma unroll
+    for (int i = 0; i < kRowBatch; ++i) O[i] = 0.f;
+    for (int s0 = 0; s0 < n_valid; s0 += kSplitBatch) {
+      float v[kRowBatch][kSplitBatch];
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) {
+        const int row = rb + i * kRowStep;
+        const float* po = a.part_o + verify_prow(a, b, kvh, row < R ? row : r0) * a.n_splits * kD + d;
+#pragma unroll
+        for (int k = 0; k < kSplitBatch; ++k)
+          v[i][k] = row < R && s0 + k < n_valid ? load_partial(&po[size_t(s0 + k) * kD]) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) {
+        const int row = rb + i * kRowStep;
+        if (row >= R) continue;
+#pragma unroll
+        for (int k = 0; k < kSplitBatch; ++k)
+          if (s0 + k < n_valid) O[i] = fmaf(sm_w[row * n_valid + s0 + k], v[i][k], O[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowBatch; ++i) {
+      const int row = rb + i * kRowStep;
+      if (row < R) out[verify_prow(a, b, kvh, row) * kD + d] = f32_to_bf16(O[i]);
+    }
   }
 }
 
@@ -304,7 +337,301 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyArgs a) {
   if (n_valid == 1) return;
 #if MASW_SPLIT_MERGE != 0
   if (!split_arrive(&a.counters[unit], n_valid, &sm_last)) return;
-  merge_verify_partials(a, b, kvh, R, n_valid);
+  merge_verify_partials(a, b, kvh, R, n_valid, reinterpret_cast<float*>(sKV));
+  if (threadIdx.x == 0) reset_ticket(&a.counters[unit]);
+#else
+  (void)sm_last;
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Streaming variant (default): every wave owns a contiguous key range of the split and
+// streams it through two private LDS stages filled by asynchronous global->LDS copies,
+// so the loop has no work-group barrier and two 32-key tiles (32 KB) per wave stay in
+// flight while the matrix cores work on the current one.
+//   stage = 16 copies of 64 lanes x 16 bytes: K rows of the tile, then V rows; row
+//   `row` of the tile is 256 contiguous bytes whose 16-byte slot s holds the row's
+//   chunk s ^ (row & 15) (the swizzle is chosen through the global address each lane
+//   fetches), so the K-operand reads (32 rows, one chunk each) hit 16 distinct slots.
+// Each wave computes all NB row blocks for its keys; the waves then merge through LDS.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* vlds_ptr_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t vlds_v4i16_t;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float vf32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 vbf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(vf32x2_t{lo, hi}, vbf16x2_t));
+}
+constexpr int kVWaveKeys = 32;                        // keys per wave tile
+constexpr int kVStageInstr = 2 * kVWaveKeys * kD * 2 / 1024;   // 16 copies of 1 KB
+constexpr int kVStageU4 = kVStageInstr * kWave;       // 16-byte words per stage
+constexpr int kVSplitRound = kVWaves * kVWaveKeys;    // keys per split rounding unit
+constexpr int vwait_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+constexpr int kVWaitLgkm0 = 0xf | (0x3 << 14) | (0x7 << 4);
+
+__device__ __forceinline__ void verify_issue(u32x4_t* stage, const uint16_t* kbase, const uint16_t* vbase, int tile,
+                                             int k1, int lane) {
+  const int sub = lane >> 4, slot = lane & 15;
+#pragma unroll
+  for (int q = 0; q < kVWaveKeys / 4; ++q) {
+    const int row = 4 * q + sub;
+    const int key = min(tile + row, k1 - 1);   // rows past the range re-read the last key (masked)
+    const int chunk = slot ^ (row & 15);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + size_t(key) * kD + chunk * 8),
+                                     (vlds_ptr_t)(stage + q * kWave), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + size_t(key) * kD + chunk * 8),
+                                     (vlds_ptr_t)(stage + (kVWaveKeys / 4 + q) * kWave), 16, 0, 0);
+  }
+}
+
+template <int NB>
+__global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyArgs a) {
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int G = a.Hq / a.Hkv;
+  const int R = G * a.n_q;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  __shared__ u32x4_t vpipe[kVWaves][2][kVStageU4];   // 128 KB; reused by the wave merge
+  __shared__ float sm_ml[kVWaves][NB * 32][2];
+  __shared__ int sm_last;
+
+  const int t = a.seq_len[b];
+  // Q^T operand (B of S^T = K Q^T): lane holds row rb*32 + l32, d = 16 ks + 8 half .. +7.
+  // One row block keeps it in registers; two read it from padded LDS rows per step
+  // (registers would not hold both blocks' accumulators and fragments).
+  constexpr bool kQRegs = NB == 1;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[kQRegs ? 8 : NB * 32 * kRS];
+  u32x4_t bq[kQRegs ? 8 : 1];
+  if constexpr (kQRegs) {
+    const int row = l32;
+    const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((size_t(b) * a.n_q + (row < R ? j : 0)) * a.Hq + size_t(kvh) * G + (row < R ? g : 0)) * kD;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      bq[ks] = row < R ? *reinterpret_cast<const u32x4_t*>(qrow + ks * 16 + half * 8) : u32x4_t{0, 0, 0, 0};
+  } else {
+    for (int c = threadIdx.x; c < NB * 32 * 16; c += kVThreads) {
+      const int row = c >> 4, ch = c & 15;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (row < R) {
+        const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
+        v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) +
+                                              ((size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g) * kD + ch * 8);
+      }
+      *reinterpret_cast<u32x4_t*>(sQ + row * kRS + ch * 8) = v;
+    }
+    __syncthreads();
+  }
+  if (t < a.n_q || t > a.max_len) {
+    if (split == 0 && kvh == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SEQ_RANGE);
+    return;
+  }
+  const int n = t;
+  const int chunk = verify_chunk(n, a.n_splits, kVSplitRound);
+  const int k0 = split * chunk;
+  if (k0 >= n) return;
+  const int k1 = min(k0 + chunk, n);
+  const int n_valid = (n + chunk - 1) / chunk;
+  const int sub = chunk / kVWaves;
+  const int w0 = k0 + wave * sub;
+  const int w1 = min(w0 + sub, k1);
+  const int nt = w0 < w1 ? (w1 - w0 + kVWaveKeys - 1) / kVWaveKeys : 0;
+
+  // causal limit of this lane's rows: last key (0-based) query j may see
+  int lim[NB];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int rho = rb * 32 + l32;
+    lim[rb] = rho < R ? t - a.n_q + (rho - (rho / a.n_q) * a.n_q) : -1;
+  }
+
+  const size_t unit = size_t(b) * a.Hkv + kvh;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + unit * a.max_len * kD;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + unit * a.max_len * kD;
+
+  f32x16_t o[NB][4];
+  float m[NB], l[NB];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[rb][db][v] = 0.f;
+  }
+
+  if (nt > 0) verify_issue(vpipe[wave][0], kbase, vbase, w0, w1, lane);
+  if (nt > 1) verify_issue(vpipe[wave][1], kbase, vbase, w0 + kVWaveKeys, w1, lane);
+  int st = 0;
+  for (int i = 0; i < nt; ++i) {
+    if (i + 1 < nt) __builtin_amdgcn_s_waitcnt(vwait_vm(kVStageInstr));   // only tile i+1 outstanding
+    else __builtin_amdgcn_s_waitcnt(vwait_vm(0));
+    const u32x4_t* stg = vpipe[wave][st];
+    const uint16_t* vst = reinterpret_cast<const uint16_t*>(stg + kVStageU4 / 2);
+    // K operand (A of S^T): key l32, d = 16 ks + 8 half .. +7
+    u32x4_t ka[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ka[ks] = stg[l32 * 16 + ((2 * ks + half) ^ (l32 & 15))];
+    // V^T operand (A of O^T): lane (l32, half) holds d = 32 db + l32 for the keys
+    // kb+0..3 and kb+8..11 (kb = 16 step + 4 half), the order of the S^T registers.  Two
+    // transposing reads per operand: in each 16-lane group lane i, element e comes from
+    // source lane 4e + i/4, element i%4, so source lane j addresses key kb + (8) + j/4,
+    // columns 32 db + 16 (group%2) + 4 (j%4) .. +3 (half of one swizzled 16-byte slot).
+    u32x4_t va[4][2];
+    {
+      const int grp = lane >> 4, j = lane & 15;
+      const int hh = grp >> 1;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int d = db * 32 + (grp & 1) * 16 + 4 * (j & 3);
+        const int cd = d >> 3, e = d & 7;
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+          uint32_t w[4];
+#pragma unroll
+          for (int part = 0; part < 2; ++part) {
+            const int key = 16 * step + 4 * hh + 8 * part + (j >> 2);
+            const uint16_t* src = vst + key * kD + ((cd ^ (key & 15)) << 3) + e;
+            const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((vlds_v4i16_t*)src);
+            const u32x2_t y = __builtin_bit_cast(u32x2_t, x);
+            w[2 * part] = y.x;
+            w[2 * part + 1] = y.y;
+          }
+          va[db][step] = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kVWaitLgkm0);
+    const int tile = w0 + i * kVWaveKeys;
+    if (i + 2 < nt) verify_issue(vpipe[wave][st], kbase, vbase, tile + 2 * kVWaveKeys, w1, lane);
+    st ^= 1;
+    const bool interior = tile + kVWaveKeys <= w1 && tile + kVWaveKeys - 1 <= t - a.n_q;
+
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      f32x16_t s;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        u32x4_t qf;
+        if constexpr (kQRegs) qf = bq[ks];
+        else qf = *reinterpret_cast<const u32x4_t*>(sQ + (rb * 32 + l32) * kRS + ks * 16 + half * 8);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+                                                    __builtin_bit_cast(bf16x8_t, qf), s, 0, 0, 0);
+      }
+      // S^T layout: register v holds key 8*(v/4) + 4*half + v%4 of the tile, row l32.
+      // Tiles below every row's causal limit and inside the range need no mask.
+      float tmax = -INFINITY;
+      if (interior) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          s[v] *= a.scale_log2;
+          tmax = fmaxf(tmax, s[v]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = tile + 8 * (v >> 2) + 4 * half + (v & 3);
+          const float sc = (key < w1 && key <= lim[rb]) ? s[v] * a.scale_log2 : -INFINITY;
+          s[v] = sc;
+          tmax = fmaxf(tmax, sc);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float mn = fmaxf(m[rb], tmax);
+      const float mref = mn == -INFINITY ? 0.f : mn;   // a row may have no key in this tile
+      const float alpha = fast_exp2(m[rb] - mref);
+      if (__any(mn != m[rb])) {   // rescale only when some row's max grew
+        l[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
+      }
+      m[rb] = mn;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(s[v] - mref);
+        s[v] = p;
+        l[rb] += p;
+      }
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+        const int v0 = 8 * step;
+        const u32x4_t pb = {cvt_pk_bf16(s[v0 + 0], s[v0 + 1]), cvt_pk_bf16(s[v0 + 2], s[v0 + 3]),
+                            cvt_pk_bf16(s[v0 + 4], s[v0 + 5]), cvt_pk_bf16(s[v0 + 6], s[v0 + 7])};
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[db][step]),
+                                                              __builtin_bit_cast(bf16x8_t, pb), o[rb][db], 0, 0, 0);
+      }
+    }
+  }
+
+  // Keys of a row are split between lanes l32 and l32 + 32: total their sums.
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) l[rb] += __shfl_xor(l[rb], 32, kWave);
+
+  // Merge the 4 waves (each holds every row over its own keys) through LDS in wave order.
+  if (half == 0) {
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      sm_ml[wave][rb * 32 + l32][0] = m[rb];
+      sm_ml[wave][rb * 32 + l32][1] = l[rb];
+    }
+  }
+  __syncthreads();   // every wave is past its loop: the stages are free
+  float* sm_o = reinterpret_cast<float*>(&vpipe[0][0][0]);   // [wave][NB*32 rows][128]
+  static_assert(kVWaves * NB * 32 * kD * 4 <= int(sizeof(vpipe)), "wave partials fit in the stages");
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int row = rb * 32 + l32;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kVWaves; ++w) M = fmaxf(M, sm_ml[w][row][0]);
+    const float wt = fast_exp2(m[rb] - (M == -INFINITY ? 0.f : M));
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        sm_o[(wave * NB * 32 + row) * kD + db * 32 + 8 * (v >> 2) + 4 * half + (v & 3)] = wt * o[rb][db][v];
+  }
+  __syncthreads();
+
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  for (int idx = threadIdx.x; idx < R * kD; idx += kVThreads) {
+    const int row = idx / kD, d = idx - (idx / kD) * kD;
+    const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
+    const size_t prow = (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
+    float Mr = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kVWaves; ++w) Mr = fmaxf(Mr, sm_ml[w][row][0]);
+    const float Mrr = Mr == -INFINITY ? 0.f : Mr;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kVWaves; ++w) {
+      L = fmaf(fast_exp2(sm_ml[w][row][0] - Mrr), sm_ml[w][row][1], L);
+      O += sm_o[(w * NB * 32 + row) * kD + d];
+    }
+    if (n_valid == 1) {
+      out[prow * kD + d] = f32_to_bf16(O / L);
+    } else {
+      const size_t pr = prow * a.n_splits + split;
+      store_partial(&a.part_o[pr * kD + d], O);
+      if (d == 0) { store_partial(&a.part_ml[pr * 2], Mr); store_partial(&a.part_ml[pr * 2 + 1], L); }
+    }
+  }
+  if (n_valid == 1) return;
+#if MASW_SPLIT_MERGE != 0
+  if (!split_arrive(&a.counters[unit], n_valid, &sm_last)) return;
+  merge_verify_partials(a, b, kvh, R, n_valid, reinterpret_cast<float*>(&vpipe[0][0][0]));
   if (threadIdx.x == 0) reset_ticket(&a.counters[unit]);
 #else
   (void)sm_last;
@@ -338,7 +665,16 @@ __global__ __launch_bounds__(kD) void verify_combine_kernel(const VerifyArgs a, 
 int launch_verify_mfma(const VerifyArgs& a, hipStream_t s) {
   const int rows = a.Hq / a.Hkv * a.n_q;
   int tk;
-  if (rows <= 32) {
+  if (kVerifyStream) {
+    if (rows <= 32) {
+      hipLaunchKernelGGL(verify_stream_kernel<1>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
+    } else if (rows <= kMaxRows) {
+      hipLaunchKernelGGL(verify_stream_kernel<2>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
+    } else {
+      return MASW_ERR_SHAPE;
+    }
+    tk = kVSplitRound;
+  } else if (rows <= 32) {
     hipLaunchKernelGGL(verify_kernel<1>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
     tk = VTile<1>::TK;
   } else if (rows <= kMaxRows) {

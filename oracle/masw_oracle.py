@@ -33,7 +33,12 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
 * R4  g_m does not attend to itself unless ``include_self`` is set.
 * R5  The slot's query vector q_g is an input (only K/V are mirrored, Algorithm 1 step 3).
 * R6  No rotary embedding on this path (all workloads draw post-positional K/V).
-* R7  1 <= r <= W.
+* R7  1 <= r <= W for a memory with a slot chain.
+* R8  r = 0 means no slot chain: the memory is sinks ++ the exact W-window, the
+      sink-plus-window structure [TR] §3.1's sink bullet takes from StreamingLLM; with
+      S = 0 it is the pure sliding window [TR] §3 opens with, which is also [TR] §4's SWA
+      baseline (1,024-token window).  No slot is ever visible, the ring keeps C = W rows
+      and every append is legal.
 
 Precision: every score, softmax and weighted sum is computed in fp64 on the stored
 input values.  Stored slot K/V in a bf16 cache are rounded to bf16 with
@@ -65,22 +70,31 @@ def local_positions(t: int, S: int, W: int) -> List[int]:
 
 
 def visible_slot_count(t: int, S: int, W: int, r: int) -> int:
-    """Slots visible at step t: one per r raw tokens that have left sink and window (reading R2)."""
+    """Slots visible at step t: one per r raw tokens that have left sink and window
+    (reading R2); none without a slot chain (r = 0, reading R8)."""
+    if r == 0:
+        return 0
     return max(0, t - S - W) // r
 
 
 def block_positions(m: int, S: int, r: int) -> List[int]:
     """Raw positions that slot g_m compresses (reading R3): S+(m-1)r+1 .. S+mr."""
+    if r == 0:
+        raise ValueError("no slot chain (r = 0)")
     return list(range(S + (m - 1) * r + 1, S + m * r + 1))
 
 
 def boundary_step(m: int, S: int, W: int, r: int) -> int:
     """Step t_m at which g_m is materialized and becomes visible (reading R3)."""
+    if r == 0:
+        raise ValueError("no slot chain (r = 0)")
     return S + W + m * r
 
 
 def is_boundary(t: int, S: int, W: int, r: int) -> int:
     """Return m if step t is the materialization step of slot m, else 0."""
+    if r == 0:
+        return 0
     d = t - S - W
     if d >= r and d % r == 0:
         return d // r
@@ -199,8 +213,8 @@ class DraftMemory:
 
     def __init__(self, S: int, W: int, r: int, n_kv_heads: int, head_dim: int,
                  bf16_cache: bool):
-        if not (1 <= r <= W) or S < 0:
-            raise ValueError("need S >= 0 and 1 <= r <= W (reading R7)")
+        if not (0 <= r <= W) or S < 0 or W < 1:
+            raise ValueError("need S >= 0, W >= 1 and 1 <= r <= W, or r = 0 (readings R7, R8)")
         self.S, self.W, self.r = S, W, r
         self.Hkv, self.D = n_kv_heads, head_dim
         self.bf16 = bf16_cache
@@ -277,7 +291,8 @@ class DraftMemory:
 # ---------------------------------------------------------------------------
 
 def ring_capacity(W: int, r: int) -> int:
-    """A block leaves the window r-1 steps before its slot exists, so the ring keeps W + r rows."""
+    """A block leaves the window r-1 steps before its slot exists, so the ring keeps W + r
+    rows; without a slot chain (r = 0) the window alone, W rows."""
     return W + r
 
 
@@ -302,6 +317,8 @@ def append_is_legal(i: int, n_slots: int, S: int, W: int, r: int) -> bool:
     """Writing raw position i may only overwrite a token whose block already has its slot."""
     if i <= S:
         return True
+    if r == 0:
+        return True            # nothing waits for a slot (reading R8)
     prev = i - ring_capacity(W, r)
     if prev <= S:
         return True
@@ -370,7 +387,7 @@ def dense_mask_decode(q_head: np.ndarray, raw_k: np.ndarray, raw_v: np.ndarray,
     for i in range(1, t + 1):
         allowed[i - 1] = (i <= S) or (i > S and i > t - W)
     m = 1
-    while m <= slot_k.shape[0]:
+    while r > 0 and m <= slot_k.shape[0]:
         if S + W + m * r <= t:
             allowed[t + m - 1] = True
         m += 1

@@ -112,6 +112,16 @@ def test_window_hand_example():
         assert keys == [("raw", i) for i in c["raw"]] + [("slot", m) for m in c["slots"]]
 
 
+def test_no_slot_window_hand_example():
+    """Reading R8: without a slot chain the memory is sinks ++ the exact window."""
+    g = _load("no_slot_window_hand_example.json")
+    for mem in g["memories"]:
+        S, W = mem["S"], mem["W"]
+        for c in mem["cases"]:
+            assert O.keylist(c["t"], S, W, 0) == [("raw", i) for i in c["raw"]], (S, W, c)
+            assert O.expected_ring(c["t"], S, W, 0) == c["ring"], (S, W, c)
+
+
 def test_tiny_workload_counts():
     g = _load("memory_counts.json")["tiny_workload"]
     S, W, r, t = g["S"], g["W"], g["r"], g["t"]
@@ -150,7 +160,7 @@ def test_worked_example_divergence_is_documented():
 def _invariant_grid():
     for S in (0, 1, 4, 7):
         for W in (1, 3, 8, 32):
-            for r in (1, 2, 5, 16, 32):
+            for r in (0, 1, 2, 5, 16, 32):
                 if r <= W:
                     yield S, W, r
 
@@ -158,14 +168,16 @@ def _invariant_grid():
 @pytest.mark.parametrize("S,W,r", list(_invariant_grid()))
 def test_keylist_invariants(S, W, r):
     C = O.ring_capacity(W, r)
-    for t in range(1, S + W + 6 * r + 3):
+    for t in range(1, S + W + 6 * max(r, 4) + 3):
         keys = O.keylist(t, S, W, r)
         n = O.visible_slot_count(t, S, W, r)
         raw = [i for k, i in keys if k == "raw"]
         slots = [m for k, m in keys if k == "slot"]
-        # I1 exact size; I2 the page's working-set bound
+        # I1 exact size; I2 the page's working-set bound (no slot chain: sinks + window)
         assert len(keys) == min(t, S) + min(max(t - S, 0), W) + n
-        assert len(keys) <= S + W + t // r
+        assert len(keys) <= S + W + (t // r if r else 0)
+        if r == 0:
+            assert n == 0 and not O.is_boundary(t, S, W, r)
         # I3 local part by enumeration straight from Eq. 4
         local = [i for i in range(1, t + 1) if i > S and max(S + 1, t - W + 1) <= i <= t]
         assert raw == list(range(1, min(S, t) + 1)) + local
@@ -178,15 +190,16 @@ def test_keylist_invariants(S, W, r):
             assert not set(O.block_positions(m, S, r)) & set(raw)
         # every non-sink raw token older than the window has left it for good:
         # its block's slot is visible, or the block is still waiting (< r steps)
+        # (without a slot chain it is simply gone: reading R8)
         for i in range(S + 1, t + 1):
-            if i not in raw:
+            if i not in raw and r:
                 m = -(-(i - S) // r)
                 assert m in slots or O.boundary_step(m, S, W, r) > t
                 assert O.boundary_step(m, S, W, r) - t < r
         # the ring keeps every visible raw token
         assert t - C < (local[0] if local else t + 1)
     # I6 the slot query sees exactly what the decode query saw r steps before
-    for m in range(1, 6):
+    for m in range(1, 6 if r else 1):
         assert O.slot_query_keylist(m, S, W, r) == O.keylist(S + W + (m - 1) * r, S, W, r)
 
 
@@ -207,7 +220,7 @@ def test_keylist_property(S, W, r, t):
 # Ring placement and append legality (bookkeeping behind the key list)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("S,W,r", [(0, 1, 1), (4, 32, 16), (2, 3, 2), (7, 8, 5), (1, 5, 5)])
+@pytest.mark.parametrize("S,W,r", [(0, 1, 1), (4, 32, 16), (2, 3, 2), (7, 8, 5), (1, 5, 5), (4, 8, 0), (0, 5, 0)])
 def test_ring_closed_form_vs_fifo_simulation(S, W, r):
     """A literal FIFO of C cells: the next free cell advances by one per non-sink token."""
     C = O.ring_capacity(W, r)
@@ -248,6 +261,17 @@ def test_append_legality_schedule(S, W, r):
         assert O.append_is_legal(tm + 1, m, S, W, r)
 
 
+@pytest.mark.parametrize("S,W", [(4, 8), (0, 5), (3, 1)])
+def test_no_slot_chain_appends_are_always_legal(S, W):
+    """Reading R8: without a slot chain no block waits for a slot; the ring keeps W rows
+    and the window is exactly what it holds."""
+    assert O.ring_capacity(W, 0) == W
+    for i in range(1, S + 5 * W + 3):
+        assert O.append_is_legal(i, 0, S, W, 0)
+        held = set(c for c in O.expected_ring(i, S, W, 0) if c is not None)
+        assert held == set(range(max(S + 1, i - W + 1), i + 1))
+
+
 def test_ring_capacity_is_tight():
     """With one cell fewer than W + r the slot query's window is no longer resident."""
     S, W, r = 4, 32, 16
@@ -262,12 +286,12 @@ def test_ring_capacity_is_tight():
 # Brute force: dense masks over every entry ever created vs the key-list oracle
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("S,W,r", [(4, 32, 16), (0, 5, 2), (3, 4, 4), (2, 6, 1), (1, 8, 3)])
+@pytest.mark.parametrize("S,W,r", [(4, 32, 16), (0, 5, 2), (3, 4, 4), (2, 6, 1), (1, 8, 3), (4, 8, 0), (0, 6, 0)])
 def test_dense_mask_bruteforce(S, W, r):
     rng = np.random.default_rng(7)
     D, Hkv, hidden = 8, 2, 8
     G = 2
-    T = S + W + 5 * r + 3
+    T = S + W + 5 * max(r, 4) + 3
     raw_k = rng.normal(size=(T, Hkv, D))
     raw_v = rng.normal(size=(T, Hkv, D))
     wk = rng.normal(size=(hidden, Hkv * D)) / 3

@@ -6,7 +6,8 @@
 // is materialized and the slot query still reads it; overwriting a row therefore
 // evicts the token i-(W+r), which is legal only once that token's block has its slot.
 // Each thread moves one 16-byte packet of K and of V; all packets of one token take
-// the same decision, so an illegal token is skipped whole.
+// the same decision (append_fate), so an illegal token is skipped whole, and so is a
+// token a later position of the same call overwrites.
 #include "masw_internal.hpp"
 
 namespace masw {
@@ -40,11 +41,9 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
       dk = static_cast<T*>(a.k_sink);
       dv = static_cast<T*>(a.v_sink);
     } else {
-      const int prev = i - a.g.C;   // the token this row held before
-      if (prev > a.g.S && a.n_slots[b] < (prev - a.g.S + a.g.r - 1) / a.g.r) {
-        bits |= MASW_DEV_PENDING_SLOT;
-        continue;
-      }
+      const AppendFate f = append_fate(i, t, a.n_slots ? a.n_slots[b] : 0, a.g);
+      if (f == kAppendIllegal) bits |= MASW_DEV_PENDING_SLOT;
+      if (f != kAppendWrite) continue;
       off = (unit * a.g.C + (i - a.g.S - 1) % a.g.C) * a.D + d;
       dk = static_cast<T*>(a.k_ring);
       dv = static_cast<T*>(a.v_ring);

@@ -28,7 +28,7 @@ int check_dims(const masw_dims* d, bool masw_memory) {
   if (d->head_dim != 64 && d->head_dim != 128) return MASW_ERR_SHAPE;
   if (d->num_splits < 0 || d->num_splits > kMaxSplits) return MASW_ERR_ARG;
   if (masw_memory) {
-    if (d->sink < 0 || d->window < 1 || d->interval < 1 || d->interval > d->window || d->max_slots < 0)
+    if (d->sink < 0 || d->window < 1 || d->interval < 0 || d->interval > d->window || d->max_slots < 0)
       return MASW_ERR_ARG;
   }
   return MASW_OK;
@@ -296,6 +296,7 @@ MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, cons
   if ((st = check_layer(d, L))) return st;
   if (!seq || !seq->seq_len || !seq->err || !h || !w_k_g || !w_v_g || !q_slot || !o_slot || hidden < 1)
     return MASW_ERR_ARG;
+  if (d->interval == 0) return MASW_ERR_ARG;   // no slot chain to materialize
   if (d->dtype == MASW_BF16 && hidden % 8) return MASW_ERR_SHAPE;
   const int splits = choose_splits(d, masw_max_keys(d));
   const WsPlan p = plan_workspace(d, splits, d->n_q_heads, true);

@@ -148,11 +148,9 @@ __device__ void append_rows(const DecodeArgs& a, int b, int kvh, int t, int have
       dk = static_cast<T*>(a.wk[0]);
       dv = static_cast<T*>(a.wv[0]);
     } else {
-      const int prev = i - a.g.C;
-      if (prev > a.g.S && have < (prev - a.g.S + a.g.r - 1) / a.g.r) {
-        bits |= MASW_DEV_PENDING_SLOT;
-        continue;
-      }
+      const AppendFate f = append_fate(i, t, have, a.g);
+      if (f == kAppendIllegal) bits |= MASW_DEV_PENDING_SLOT;
+      if (f != kAppendWrite) continue;
       off = (unit * a.g.C + (i - a.g.S - 1) % a.g.C) * D + d;
       dk = static_cast<T*>(a.wk[1]);
       dv = static_cast<T*>(a.wv[1]);

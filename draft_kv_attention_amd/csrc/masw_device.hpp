@@ -143,8 +143,8 @@ __device__ __forceinline__ void reset_ticket(int32_t* counter) {
 struct MemGeom {
   int S;          // sink count (a full cache is a memory whose every token is a sink)
   int W;          // local window
-  int r;          // slot interval
-  int C;          // ring rows, W + r
+  int r;          // slot interval; 0 = no slot chain (sinks + window only)
+  int C;          // ring rows, W + r (W without a slot chain)
   int max_slots;  // slot rows per (sequence, KV head)
 };
 
@@ -161,9 +161,31 @@ __device__ __forceinline__ KeySpan key_span(int t, const MemGeom& g) {
   k.nl = min(max(t - g.S, 0), g.W);
   k.lo = t - k.nl + 1;
   int d = t - g.S - g.W;
-  k.nslot = d > 0 ? d / g.r : 0;
+  k.nslot = d > 0 && g.r > 0 ? d / g.r : 0;   // r = 0: no slot chain
   k.ring0 = k.nl > 0 ? (k.lo - g.S - 1) % g.C : 0;
   return k;
+}
+
+// Raw append ([TR] §3.2 Algorithm 1 step 5).  Writing non-sink position i into ring row
+// (i-S-1) mod C evicts the token `victim` = i - C held there; that is legal once the
+// victim's block has its slot (always without a slot chain, or for a sink/never-written
+// row).
+__device__ __forceinline__ bool evict_ok(int victim, int have, const MemGeom& g) {
+  return victim <= g.S || g.r == 0 || have >= (victim - g.S + g.r - 1) / g.r;
+}
+
+enum AppendFate { kAppendWrite = 0, kAppendSuperseded = 1, kAppendIllegal = 2 };
+
+// Fate of non-sink position i in an append call whose newest position is t, with `have`
+// slots materialized.  A call may hold more than C positions; read sequentially, the
+// positions landing in one row are written in order, and legality along that chain is
+// monotone (each evicts a later token than the one before), so i's write is final iff
+// it is legal and the next position of the chain (i + C, if in this call) does not
+// legally overwrite it.  Illegal writes are suppressed and reported.
+__device__ __forceinline__ AppendFate append_fate(int i, int t, int have, const MemGeom& g) {
+  if (!evict_ok(i - g.C, have, g)) return kAppendIllegal;
+  if (i + g.C <= t && evict_ok(i, have, g)) return kAppendSuperseded;
+  return kAppendWrite;
 }
 
 struct KeyRef {

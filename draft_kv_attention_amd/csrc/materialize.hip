@@ -17,7 +17,7 @@ namespace {
 __device__ __forceinline__ int boundary_slot(const ProjectArgs& a, int b, int& bits) {
   const int t = a.seq_len[b];
   const int d = t - a.g.S - a.g.W;
-  if (d < a.g.r || d % a.g.r) return 0;
+  if (a.g.r < 1 || d < a.g.r || d % a.g.r) return 0;   // r = 0: no slot chain
   const int m = d / a.g.r;
   const int have = a.n_slots[b];
   if (have == m) return 0;

@@ -85,7 +85,11 @@ typedef struct {
   int32_t head_dim;    /* D in {64, 128}                                           */
   int32_t sink;        /* S >= 0                                                   */
   int32_t window;      /* W >= 1                                                   */
-  int32_t interval;    /* r, 1 <= r <= W; the local ring holds C = W + r rows       */
+  int32_t interval;    /* r, 1 <= r <= W; the local ring holds C = W + r rows.
+                          r = 0: no slot chain - sinks ++ the exact W-window only
+                          (StreamingLLM-style with S > 0, a sliding window with
+                          S = 0); the ring holds C = W rows and every append is
+                          legal; masw_materialize_slot returns MASW_ERR_ARG        */
   int32_t max_slots;   /* slot rows allocated per (sequence, KV head), >= 0         */
   int32_t dtype;       /* masw_dtype of every K/V/q/out/h/w tensor                 */
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(D) ([TR] §2.3 Eq. 2)  */
@@ -130,8 +134,8 @@ enum {
  * evicts the token i-(W+r) that occupied it.  That eviction is legal only if the
  * evicted token is a never-written cell or its block's slot already exists
  * (n_slots[b] >= ceil((i-(W+r)-S)/r)); otherwise the token is not written and
- * MASW_DEV_PENDING_SLOT is set.  t < n_new sets MASW_DEV_SEQ_RANGE and writes nothing.
- * n_new == 0 is a no-op. */
+ * MASW_DEV_PENDING_SLOT is set.  Without a slot chain (r = 0) every eviction is legal.
+ * t < n_new sets MASW_DEV_SEQ_RANGE and writes nothing.  n_new == 0 is a no-op. */
 MASW_API int masw_evict_append(const masw_dims* dims, const masw_layer* layer,
                                const masw_seq* seq, const void* k_new, const void* v_new,
                                int32_t n_new, hipStream_t stream);

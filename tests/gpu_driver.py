@@ -87,6 +87,10 @@ class LayerDriver:
     def advance_to(self, t_target: int, include_self: bool = False, on_slot=None):
         """Append up to t_target, materializing at every boundary on the way."""
         S, W, r = self.shape.sink, self.shape.window, self.shape.interval
+        if r == 0:                       # no slot chain: nothing to materialize
+            if self.t < t_target:
+                self.append(t_target - self.t)
+            return
         while self.t < t_target:
             if self.t < S + W:
                 nxt = S + W + r

@@ -47,7 +47,7 @@ def _dims(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(interval=0), -1), (dict(interval=2049), -1), (dict(sink=-1), -1), (dict(max_slots=-1), -1),
+    (dict(interval=-1), -1), (dict(interval=2049), -1), (dict(sink=-1), -1), (dict(max_slots=-1), -1),
     (dict(n_q_heads=20), -3), (dict(head_dim=96), -3), (dict(n_q_heads=40, n_kv_heads=8), -3),
     (dict(dtype=7), -2), (dict(num_splits=257), -1), (dict(batch=0), -3)])
 def test_invalid_dims_rejected_on_host(lib, kw, status):
@@ -85,6 +85,16 @@ def test_stream_read_rejects_bad_sizes_on_host(lib):
     assert lib.masw_stream_read(1 << 20, 24, 0, 1 << 20, None) == -1
     assert lib.masw_stream_read((1 << 20) + 4, 32, 0, 1 << 20, None) == -1
     assert lib.masw_stream_read(1 << 20, 32, -1, 1 << 20, None) == -1
+
+
+def test_no_slot_chain_has_nothing_to_materialize(lib):
+    """interval 0 (sinks + window only) is a valid memory, but materialization is not."""
+    d = _dims(interval=0, max_slots=0)
+    assert lib.masw_workspace_bytes(ctypes.byref(d), M.OP_DRAFT_ATTN, 0, 0) > 0
+    layer = M._Layer(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    seq = M._Seq(1 << 20, 1 << 20)
+    assert lib.masw_materialize_slot(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq), 3072,
+                                     1, 1, 1, 1, 1, 0, 1 << 20, 1 << 30, None) == -1
 
 
 def test_workspace_sizes(lib):

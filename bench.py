@@ -22,6 +22,7 @@ device value is read inside the timed region.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -49,7 +50,7 @@ T_HEAD = 32768
 
 
 def n_slots_at(t, S, W, r):
-    return max(0, t - S - W) // r
+    return max(0, t - S - W) // r if r else 0   # r = 0: no slot chain
 
 
 def keys_at(t, S, W, r):
@@ -58,7 +59,7 @@ def keys_at(t, S, W, r):
 
 def is_boundary(t, S, W, r):
     d = t - S - W
-    return d >= r and d % r == 0
+    return r > 0 and d >= r and d % r == 0
 
 
 class Stack:
@@ -164,7 +165,7 @@ class Stack:
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for name, fn in (("masw", lambda: self.masw_step(False)),
-                             ("masw_boundary", lambda: self.masw_step(True)),
+                             ("masw_boundary", (lambda: self.masw_step(True)) if self.r else None),
                              ("full", self.full_step if self.kf else None)):
                 if fn is None:
                     continue
@@ -272,6 +273,32 @@ def stream_read_leg(dev, launch_bytes, reps=5):
                 launch_size_bytes=int(n16), launch_size_us=round(us_small, 2),
                 launch_size_gbs=round(n16 / us_small / 1e3, 1),
                 launch_size_pct_peak=round(100 * n16 / us_small / 1e3 / HBM_PEAK_GBS, 1))
+
+
+SECOND_WORKLOADS = (("paper_w128_s128_r4", 128, 128, 4), ("paper_w128_s128_r8", 128, 128, 8),
+                    ("swa_w1024", 0, 1024, 0), ("sink4_window2048", 4, 2048, 0))
+
+
+def second_workload_leg(dev, prefixes=(8192, 16384, 32768), steps=32, warmup=4):
+    """The paper's own memory geometry (W = S = 128, r = 4 / 8 raw tokens per slot) and
+    memories without a slot chain (a 1,024-token sliding window, sinks + window) through
+    the same kernels, at the 3B draft shapes, B = 8: graph-replayed 28-layer steps with
+    boundary steps (slot materialization) where the geometry has them."""
+    out = []
+    for name, S, W, r in SECOND_WORKLOADS:
+        shape = dataclasses.replace(SHAPE, sink=S, window=W, interval=r)
+        st = Stack(shape, max(prefixes) + steps + warmup + 8, dev, seed=3, with_full=False)
+        st.capture()
+        for t in prefixes:
+            ms, nb = time_steps(st, "masw", t, warmup, steps)
+            out.append(dict(workload=name, sink=S, window=W, interval=r, prefix=t,
+                            keys=keys_at(t, S, W, r), ms=round(ms, 4), steps_per_s=round(1e3 / ms, 2),
+                            gbs=round(nb / (ms * 1e-3) / 1e9, 1),
+                            pct_peak=round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)))
+        assert int(st.seq.err.item()) == 0, name
+        del st
+        torch.cuda.empty_cache()
+    return out
 
 
 def single_sequence_leg(dev, steps=64, warmup=10):
@@ -579,6 +606,9 @@ def main():
     print(f"[bench] verifier {ver}", file=sys.stderr, flush=True)
     single = single_sequence_leg(dev)
     print(f"[bench] batch-1 prefix-8192 {single}", file=sys.stderr, flush=True)
+    second = None if args.no_sweep else second_workload_leg(dev)
+    for row in second or ():
+        print(f"[bench] second workload {row}", file=sys.stderr, flush=True)
     sread = stream_read_leg(dev, roof["bytes_per_launch"])
     print(f"[bench] streaming read {sread}", file=sys.stderr, flush=True)
 
@@ -601,7 +631,7 @@ def main():
         "hbm_gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(value * sh.batch, 1),
         "fullkv_at_prefix": full_head, "sweep": sweep, "eq3_fit": fits, "device_err_bits": err_bits,
-        "batch1_prefix8192": single, "streaming_read": sread,
+        "batch1_prefix8192": single, "second_workloads": second, "streaming_read": sread,
         "materialization": mat, "verifier": ver,
         "roofline": roof, "cpu_baseline": cpu,
     }

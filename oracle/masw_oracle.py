@@ -39,6 +39,13 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
       S = 0 it is the pure sliding window [TR] §3 opens with, which is also [TR] §4's SWA
       baseline (1,024-token window).  No slot is ever visible, the ring keeps C = W rows
       and every append is legal.
+* R9  Rollback ([TR] §3.3 Algorithm 2 step 6): after the target accepts the first L_acc
+      of the draft's candidates, the memory is what appending only the accepted tokens
+      would have built: raw tokens past the accepted length t_acc are dropped and so is
+      every slot materialized strictly after t_acc.  The retained raw-KV rollback window
+      is read as `rollback` extra ring rows (C = W + r + rollback): a speculative append
+      at position i <= t_acc + rollback evicts i - C <= t_acc - W - r, a token the memory
+      at t_acc no longer needs, so undoing speculation moves no data.
 
 Precision: every score, softmax and weighted sum is computed in fp64 on the stored
 input values.  Stored slot K/V in a bf16 cache are rounded to bf16 with
@@ -264,6 +271,18 @@ class DraftMemory:
         K, V = self.gather(keys)
         return gqa_attend(np.asarray(q_slot, np.float64), K, V, scale)
 
+    def rollback(self, t_acc: int) -> None:
+        """Undo speculation past the accepted length t_acc (reading R9, [TR] §3.3
+        Algorithm 2 step 6): drop raw tokens after t_acc and every slot materialized
+        strictly after t_acc."""
+        if not 0 <= t_acc <= self.t:
+            raise ValueError("rollback target outside 0..t")
+        for i in [i for i in self.raw if i > t_acc]:
+            del self.raw[i]
+        for m in [m for m in self.slots if boundary_step(m, self.S, self.W, self.r) > t_acc]:
+            del self.slots[m]
+        self.t = t_acc
+
     # -- reads -------------------------------------------------------------
     def gather(self, keys: Sequence[Key]) -> Tuple[np.ndarray, np.ndarray]:
         """Stack the K/V of the listed entries into [Hkv][n][D]."""
@@ -290,20 +309,21 @@ class DraftMemory:
 # Physical placement used by the bookkeeping checks (reading R3 / invariant I8)
 # ---------------------------------------------------------------------------
 
-def ring_capacity(W: int, r: int) -> int:
+def ring_capacity(W: int, r: int, rollback: int = 0) -> int:
     """A block leaves the window r-1 steps before its slot exists, so the ring keeps W + r
-    rows; without a slot chain (r = 0) the window alone, W rows."""
-    return W + r
+    rows; without a slot chain (r = 0) the window alone, W rows; plus the rollback rows
+    that keep speculative appends undoable (reading R9)."""
+    return W + r + rollback
 
 
-def ring_cell(i: int, S: int, W: int, r: int) -> int:
-    """Ring row of non-sink raw position i: (i - S - 1) mod (W + r)."""
-    return (i - S - 1) % ring_capacity(W, r)
+def ring_cell(i: int, S: int, W: int, r: int, rollback: int = 0) -> int:
+    """Ring row of non-sink raw position i: (i - S - 1) mod C."""
+    return (i - S - 1) % ring_capacity(W, r, rollback)
 
 
-def expected_ring(t: int, S: int, W: int, r: int) -> List[Optional[int]]:
+def expected_ring(t: int, S: int, W: int, r: int, rollback: int = 0) -> List[Optional[int]]:
     """Closed form (I8): cell c holds the largest position i <= t, i > S, with ring_cell(i) = c."""
-    C = ring_capacity(W, r)
+    C = ring_capacity(W, r, rollback)
     cells: List[Optional[int]] = [None] * C
     for c in range(C):
         i_first = S + 1 + c
@@ -313,13 +333,13 @@ def expected_ring(t: int, S: int, W: int, r: int) -> List[Optional[int]]:
     return cells
 
 
-def append_is_legal(i: int, n_slots: int, S: int, W: int, r: int) -> bool:
+def append_is_legal(i: int, n_slots: int, S: int, W: int, r: int, rollback: int = 0) -> bool:
     """Writing raw position i may only overwrite a token whose block already has its slot."""
     if i <= S:
         return True
     if r == 0:
         return True            # nothing waits for a slot (reading R8)
-    prev = i - ring_capacity(W, r)
+    prev = i - ring_capacity(W, r, rollback)
     if prev <= S:
         return True
     m = -(-(prev - S) // r)   # block of the overwritten token, ceil((prev - S) / r)

@@ -462,3 +462,109 @@ def test_project_slot_batch_rows_are_independent():
         k1, v1 = O.project_slot(H[i], wk, wv, Hkv, D, bf16_cache=True)
         np.testing.assert_array_equal(kb[i], k1)
         np.testing.assert_array_equal(vb[i], v1)
+
+
+# ---------------------------------------------------------------------------
+# Rollback after verification (reading R9, [TR] §3.3 Algorithm 2 step 6)
+# ---------------------------------------------------------------------------
+
+def _speculative_run(S, W, r, L_draft, iters, seed):
+    """Draft L_draft tokens per iteration (materializing at boundaries), accept a random
+    prefix, roll back; returns the memory and the accepted token stream."""
+    rng = np.random.default_rng(seed)
+    D, Hkv, hidden = 4, 1, 4
+    wk, wv = rng.normal(size=(hidden, Hkv * D)), rng.normal(size=(hidden, Hkv * D))
+    h_of = {m: rng.normal(size=hidden) for m in range(1, 400)}
+    q_of = {m: rng.normal(size=(1, D)) for m in range(1, 400)}
+    mem = O.DraftMemory(S, W, r, Hkv, D, bf16_cache=False)
+    accepted = []                         # (k, v) per accepted position
+    for _ in range(iters):
+        t0 = mem.t
+        draft = [(rng.normal(size=(Hkv, D)), rng.normal(size=(Hkv, D))) for _ in range(L_draft)]
+        for k, v in draft:
+            mem.append(k[None], v[None])
+            m = mem.pending_boundary()
+            if m:
+                mem.materialize(h_of[m], wk, wv, q_of[m], 0.5)
+        n_acc = int(rng.integers(0, L_draft + 1))
+        mem.rollback(t0 + n_acc)
+        accepted += draft[:n_acc]
+        # the target's correction token is the next accepted one
+        k, v = rng.normal(size=(Hkv, D)), rng.normal(size=(Hkv, D))
+        mem.append(k[None], v[None])
+        m = mem.pending_boundary()
+        if m:
+            mem.materialize(h_of[m], wk, wv, q_of[m], 0.5)
+        accepted.append((k, v))
+    return mem, accepted, (wk, wv, h_of, q_of)
+
+
+@pytest.mark.parametrize("S,W,r,L", [(2, 8, 4, 5), (0, 6, 2, 3), (4, 16, 8, 5), (1, 4, 1, 4), (3, 8, 0, 5)])
+def test_rollback_equals_appending_only_accepted_tokens(S, W, r, L):
+    mem, accepted, (wk, wv, h_of, q_of) = _speculative_run(S, W, r, L, iters=40, seed=S * 7 + W + r)
+    ref = O.DraftMemory(S, W, r, 1, 4, bf16_cache=False)
+    for k, v in accepted:
+        ref.append(k[None], v[None])
+        m = ref.pending_boundary()
+        if m:
+            ref.materialize(h_of[m], wk, wv, q_of[m], 0.5)
+    assert mem.t == ref.t == len(accepted)
+    assert sorted(mem.raw) == sorted(ref.raw) and sorted(mem.slots) == sorted(ref.slots)
+    for i in ref.raw:
+        np.testing.assert_array_equal(mem.raw[i][0], ref.raw[i][0])
+    for m in ref.slots:
+        np.testing.assert_array_equal(mem.slots[m][0], ref.slots[m][0])
+        np.testing.assert_array_equal(mem.slots[m][1], ref.slots[m][1])
+    q = np.random.default_rng(1).normal(size=(1, 4))
+    np.testing.assert_array_equal(mem.decode(q, 0.5), ref.decode(q, 0.5))
+
+
+def _ring_run(S, W, r, R, depth, seed=3):
+    """Literal FIFO ring of W + r + R cells driven through speculation of `depth`
+    positions and rollback; returns False as soon as a token the accepted memory needs
+    is not in its cell (or an append is illegal)."""
+    rng = np.random.default_rng(seed)
+    C = O.ring_capacity(W, r, R)
+    cells = [None] * C
+    t, n_slots = 0, 0
+
+    def put(i, n):
+        if i > S:
+            if not O.append_is_legal(i, n, S, W, r, R):
+                return False
+            cells[O.ring_cell(i, S, W, r, R)] = i
+        return True
+
+    def resident(t):
+        need = [i for kind, i in O.keylist(t, S, W, r) if kind == "raw" and i > S]
+        m = O.is_boundary(t, S, W, r)
+        if m:
+            need += [i for kind, i in O.slot_query_keylist(m, S, W, r) if kind == "raw" and i > S]
+        return all(cells[O.ring_cell(i, S, W, r, R)] == i for i in need)
+
+    for _ in range(60):
+        n_spec = n_slots
+        for j in range(1, depth + 1):          # speculative appends
+            if not put(t + j, n_spec) or not resident(t + j):
+                return False
+            if O.is_boundary(t + j, S, W, r):
+                n_spec += 1
+        acc = int(rng.integers(0, depth + 1))
+        for j in range(1, acc + 2):            # accepted prefix + correction, re-appended
+            if not put(t + j, n_slots) or not resident(t + j):
+                return False
+            if O.is_boundary(t + j, S, W, r):
+                n_slots += 1
+        t += acc + 1
+    return True
+
+
+@pytest.mark.parametrize("S,W,r,R", [(2, 8, 4, 5), (0, 6, 2, 3), (4, 16, 8, 16), (1, 4, 1, 4), (3, 8, 0, 5)])
+def test_rollback_rows_keep_needed_tokens_resident(S, W, r, R):
+    """With W + r + R ring rows any speculation of up to R positions can be undone without
+    moving data (R + 1 as well: the next position is always appended before the next
+    query reads); R + 2 can lose a token the next query needs (the oldest of a
+    boundary's slot-query window, or without a slot chain the oldest of the window)."""
+    assert _ring_run(S, W, r, R, depth=R)
+    assert _ring_run(S, W, r, R, depth=R + 1)
+    assert not all(_ring_run(S, W, r, R, depth=R + 2, seed=sd) for sd in range(8))

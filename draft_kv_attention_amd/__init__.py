@@ -48,7 +48,7 @@ class _Dims(ctypes.Structure):
                 ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("interval", ctypes.c_int32), ("max_slots", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("num_splits", ctypes.c_int32)]
+                ("num_splits", ctypes.c_int32), ("rollback", ctypes.c_int32)]
 
 
 class _Layer(ctypes.Structure):
@@ -83,6 +83,7 @@ _SIGS = {
     "masw_abi_version": (ctypes.c_int, []),
     "masw_debug_keylist": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P]),
     "masw_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_int32, _P, _P]),
+    "masw_rollback": (ctypes.c_int, [_P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -122,15 +123,16 @@ class Dims:
     dtype: torch.dtype = torch.bfloat16
     scale: float = 0.0
     num_splits: int = 0
+    rollback: int = 0
 
     def c(self) -> _Dims:
         return _Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.sink,
                      self.window, self.interval, self.max_slots, _DTYPES[self.dtype],
-                     float(self.scale), self.num_splits)
+                     float(self.scale), self.num_splits, self.rollback)
 
     @property
     def ring(self) -> int:
-        return self.window + self.interval
+        return self.window + self.interval + self.rollback
 
     @property
     def softmax_scale(self) -> float:
@@ -385,6 +387,16 @@ def masw_debug_keylist(d: Dims, seq: Seq, back: int = 0, max_keys: Optional[int]
 
 
 STREAM_SUMS = 256   # MASW_STREAM_SUMS
+
+
+def masw_rollback(d: Dims, layer: Layer, seq: Seq, t_spec: torch.Tensor, stream=None) -> None:
+    """Undo speculation: seq.seq_len already holds the accepted lengths, t_spec [B] int32
+    the lengths the memory reached while drafting (see include/masw.h)."""
+    _check_seq(d, seq)
+    _check(t_spec, "t_spec", (d.batch,), torch.int32)
+    dc, lc, sc = d.c(), layer.c(), seq.c()
+    _ok("masw_rollback", lib().masw_rollback(ctypes.byref(dc), ctypes.byref(lc), ctypes.byref(sc),
+                                             t_spec.data_ptr(), _stream(stream)))
 
 
 def stream_read(buf: torch.Tensor, sums: torch.Tensor, work_groups: int = 0, stream=None) -> None:

@@ -55,7 +55,32 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   if (bits) atomicOr(a.err, bits);
 }
 
+// Rollback: one thread per sequence.  The accepted memory keeps the slots materialized
+// at or before t_acc, n(t_acc) of them; the raw tokens need nothing (rollback rows).
+__global__ void rollback_kernel(const MemGeom g, int rollback, const int32_t* seq_len, const int32_t* t_spec,
+                                int32_t* n_slots, int32_t* err, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int t_acc = seq_len[b], ts = t_spec[b];
+  if (t_acc < 0 || t_acc > ts || ts - t_acc > rollback) {
+    atomicOr(err, MASW_DEV_ROLLBACK_RANGE);
+    return;
+  }
+  const int d = t_acc - g.S - g.W;
+  const int n = d > 0 && g.r > 0 ? d / g.r : 0;
+  const int have = n_slots[b];
+  if (have > n) n_slots[b] = n;
+  else if (have < n) atomicOr(err, MASW_DEV_SLOT_MISSING);
+}
+
 }  // namespace
+
+int launch_rollback(const MemGeom& g, int rollback, const int32_t* seq_len, const int32_t* t_spec,
+                    int32_t* n_slots, int32_t* err, int B, hipStream_t s) {
+  hipLaunchKernelGGL(rollback_kernel, dim3((B + 255) / 256), dim3(256), 0, s, g, rollback, seq_len, t_spec,
+                     n_slots, err, B);
+  return hipGetLastError() == hipSuccess ? MASW_OK : MASW_ERR_LAUNCH;
+}
 
 int launch_append(const AppendArgs& a, int dtype, hipStream_t s) {
   const int vec = dtype == MASW_BF16 ? 8 : 4;

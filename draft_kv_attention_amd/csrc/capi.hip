@@ -28,7 +28,8 @@ int check_dims(const masw_dims* d, bool masw_memory) {
   if (d->head_dim != 64 && d->head_dim != 128) return MASW_ERR_SHAPE;
   if (d->num_splits < 0 || d->num_splits > kMaxSplits) return MASW_ERR_ARG;
   if (masw_memory) {
-    if (d->sink < 0 || d->window < 1 || d->interval < 0 || d->interval > d->window || d->max_slots < 0)
+    if (d->sink < 0 || d->window < 1 || d->interval < 0 || d->interval > d->window || d->max_slots < 0 ||
+        d->rollback < 0 || d->rollback > kMaxRollback)
       return MASW_ERR_ARG;
   }
   return MASW_OK;
@@ -84,7 +85,7 @@ float scale_log2(const masw_dims* d) {
 }
 
 MemGeom masw_geom(const masw_dims* d) {
-  return MemGeom{d->sink, d->window, d->interval, d->window + d->interval, d->max_slots};
+  return MemGeom{d->sink, d->window, d->interval, d->window + d->interval + d->rollback, d->max_slots};
 }
 
 // A full cache is a memory in which every one of its max_len tokens is a sink.
@@ -111,7 +112,7 @@ void fill_masw_memory(DecodeArgs& a, const masw_dims* d, const masw_layer* L) {
   a.v[0] = or_else(L->v_sink, L->v_ring); a.v[1] = L->v_ring; a.v[2] = or_else(L->v_slot, L->v_ring);
   a.wk[0] = L->k_sink ? L->k_sink : L->k_ring; a.wk[1] = L->k_ring;
   a.wv[0] = L->v_sink ? L->v_sink : L->v_ring; a.wv[1] = L->v_ring;
-  a.cap[0] = d->sink; a.cap[1] = d->window + d->interval; a.cap[2] = d->max_slots;
+  a.cap[0] = d->sink; a.cap[1] = d->window + d->interval + d->rollback; a.cap[2] = d->max_slots;
   a.g = masw_geom(d);
 }
 
@@ -337,6 +338,15 @@ MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, cons
   a.out = o_slot;
   fill_common(a, d, splits, ws, p);
   return launch_decode(a, d->dtype, d->head_dim, stream);
+}
+
+MASW_API int masw_rollback(const masw_dims* d, const masw_layer* L, const masw_seq* seq, const int32_t* t_spec,
+                           hipStream_t stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if ((st = check_layer(d, L))) return st;
+  if (!seq || !seq->seq_len || !seq->err || !t_spec) return MASW_ERR_ARG;
+  return launch_rollback(masw_geom(d), d->rollback, seq->seq_len, t_spec, L->n_slots, seq->err, d->batch, stream);
 }
 
 MASW_API int fullkv_verify_attn(const masw_dims* d, const void* k, const void* v, int32_t max_len,

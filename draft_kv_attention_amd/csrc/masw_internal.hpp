@@ -120,6 +120,11 @@ struct AppendArgs {
 
 int launch_append(const AppendArgs& a, int dtype, hipStream_t s);
 
+// Rollback rows a memory may keep (ring rows are W + r + rollback).
+constexpr int kMaxRollback = 4096;
+int launch_rollback(const MemGeom& g, int rollback, const int32_t* seq_len, const int32_t* t_spec,
+                    int32_t* n_slots, int32_t* err, int B, hipStream_t s);
+
 // Mirrored projection of the slot hidden state into slot row m-1, plus the
 // per-sequence boundary decision written to `active`.
 struct ProjectArgs {

@@ -50,7 +50,7 @@ extern "C" {
 #endif
 
 #define MASW_API __attribute__((visibility("default")))
-#define MASW_ABI_VERSION 2
+#define MASW_ABI_VERSION 3
 
 /* ---- host status codes ------------------------------------------------------- */
 enum {
@@ -70,8 +70,10 @@ enum {
   MASW_DEV_SLOT_CAPACITY = 2, /* a step needs more than max_slots slots                  */
   MASW_DEV_SEQ_RANGE = 4,     /* seq_len out of range (t < 1 for a query, t < n_new for
                                  an append, t > max_len for a full cache, t < n_q ...)   */
-  MASW_DEV_SLOT_MISSING = 8   /* a query needs slot n(t) (or a boundary needs slot m-1)
+  MASW_DEV_SLOT_MISSING = 8,  /* a query needs slot n(t) (or a boundary needs slot m-1)
                                  but n_slots says it was never materialized              */
+  MASW_DEV_ROLLBACK_RANGE = 16 /* a rollback reaches further back than the rollback rows
+                                 keep (or forward); that sequence was left as it was      */
 };
 
 typedef enum { MASW_F32 = 0, MASW_BF16 = 1 } masw_dtype;
@@ -94,13 +96,17 @@ typedef struct {
   int32_t dtype;       /* masw_dtype of every K/V/q/out/h/w tensor                 */
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(D) ([TR] §2.3 Eq. 2)  */
   int32_t num_splits;  /* split-K plan: 0 = library heuristic, else splits per
-                          (sequence, KV head) in 1..256.  Two calls over the same
-                          keys with the same value give bitwise equal results.     */
+                          (sequence, KV head) in 1..256 (the MFMA verifier uses at
+                          most 64).  Two calls over the same keys with the same
+                          value give bitwise equal results.                        */
+  int32_t rollback;    /* R >= 0 extra ring rows that keep speculative appends
+                          undoable (masw_rollback): the ring holds C = W + r + R
+                          rows.  0: no rollback.                                   */
 } masw_dims;
 
-/* One layer's compact draft memory ([TR] §3.1 Eq. 4).  Layouts:
+/* One layer's compact draft memory ([TR] §3.1 Eq. 4).  Layouts (C = W + r + rollback):
  *   k_sink, v_sink [B][Hkv][S][D]      sink cell i-1 holds position i (i <= S)
- *   k_ring, v_ring [B][Hkv][W+r][D]    ring cell (i-S-1) mod (W+r) holds position i > S
+ *   k_ring, v_ring [B][Hkv][C][D]      ring cell (i-S-1) mod C holds position i > S
  *   k_slot, v_slot [B][Hkv][max_slots][D]  slot row m-1 holds g_m
  *   n_slots [B]                        slots materialized so far in THIS layer       */
 typedef struct {
@@ -179,6 +185,19 @@ MASW_API int masw_decode_step(const masw_dims* dims, const masw_layer* layer, co
                               const void* k_new, const void* v_new, int32_t n_new, const void* q,
                               void* out, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* Rollback after verification ([TR] §3.3 Algorithm 2 step 6): the target accepted the
+ * draft's candidates up to position t_acc = seq_len[b] (the caller has already set
+ * seq_len back); t_spec[b] is the length the memory reached while drafting.  The call
+ * drops every slot materialized strictly after t_acc (n_slots[b] = n(t_acc)); the raw
+ * tokens past t_acc need no action, because with C = W + r + rollback ring rows a
+ * speculative append evicts only tokens the memory at t_acc no longer needs - so the
+ * layer is then exactly what appending only the accepted tokens would have built.
+ * Requires 0 <= t_acc <= t_spec <= t_acc + rollback, else MASW_DEV_ROLLBACK_RANGE and
+ * the sequence is left alone; n_slots[b] < n(t_acc) sets MASW_DEV_SLOT_MISSING.
+ * t_spec [B] int32, device.  Call once per layer. */
+MASW_API int masw_rollback(const masw_dims* dims, const masw_layer* layer, const masw_seq* seq,
+                           const int32_t* t_spec, hipStream_t stream);
 
 /* Full-KV draft decode attention, the baseline ([TR] §2.3 Eq. 2 over K_{<=t}).
  * k, v [B][Hkv][max_len][D] (row i-1 holds position i); q, out [B][Hq][D]; keys 1..t.

@@ -47,7 +47,7 @@ def _dims(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(interval=-1), -1), (dict(interval=2049), -1), (dict(sink=-1), -1), (dict(max_slots=-1), -1),
+    (dict(interval=-1), -1), (dict(interval=2049), -1), (dict(rollback=-1), -1), (dict(sink=-1), -1), (dict(max_slots=-1), -1),
     (dict(n_q_heads=20), -3), (dict(head_dim=96), -3), (dict(n_q_heads=40, n_kv_heads=8), -3),
     (dict(dtype=7), -2), (dict(num_splits=257), -1), (dict(batch=0), -3)])
 def test_invalid_dims_rejected_on_host(lib, kw, status):
@@ -95,6 +95,16 @@ def test_no_slot_chain_has_nothing_to_materialize(lib):
     seq = M._Seq(1 << 20, 1 << 20)
     assert lib.masw_materialize_slot(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq), 3072,
                                      1, 1, 1, 1, 1, 0, 1 << 20, 1 << 30, None) == -1
+
+
+def test_rollback_rejects_bad_arguments_on_host(lib):
+    d = _dims(rollback=16)
+    layer = M._Layer(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    seq = M._Seq(1 << 20, 1 << 20)
+    assert lib.masw_rollback(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq), None, None) == -1
+    assert lib.masw_rollback(ctypes.byref(d), None, ctypes.byref(seq), 1 << 20, None) == -1
+    bad = _dims(rollback=-3)
+    assert lib.masw_rollback(ctypes.byref(bad), ctypes.byref(layer), ctypes.byref(seq), 1 << 20, None) == -1
 
 
 def test_workspace_sizes(lib):

@@ -301,6 +301,24 @@ def second_workload_leg(dev, prefixes=(8192, 16384, 32768), steps=32, warmup=4):
     return out
 
 
+def rollback_leg(dev, reps=4):
+    """masw_rollback per layer at the bench shape (B = 8, rollback rows 16, the paper's
+    retained window): truncating n_slots after a rejected speculation, graph-replayed
+    over 28 layers; the raw tokens need no data movement."""
+    sh = SHAPE
+    d = M.Dims(batch=sh.batch, n_q_heads=sh.n_q_heads, n_kv_heads=sh.n_kv_heads, head_dim=sh.head_dim,
+               sink=sh.sink, window=sh.window, interval=sh.interval, max_slots=8, dtype=sh.dtype, rollback=16)
+    layers = [M.alloc_layer(d, dev, fill=None) for _ in range(sh.layers)]
+    seq = M.alloc_seq(sh.batch, dev)
+    seq.seq_len.fill_(sh.sink + sh.window + 5 * sh.interval)
+    t_spec = seq.seq_len + 5
+    for lay in layers:
+        lay.n_slots.fill_(6)
+    us = graph_per_call_us(lambda i: M.masw_rollback(d, layers[i % sh.layers], seq, t_spec), sh.layers * reps)
+    ok = int(seq.err.item()) == 0 and all(int(l.n_slots[0].item()) == 5 for l in layers)
+    return dict(op="masw_rollback", us_per_layer=round(us, 2), rollback_rows=16, batch=sh.batch, checked=ok)
+
+
 def single_sequence_leg(dev, steps=64, warmup=10):
     """BASELINE configuration 1: one sequence at prefix 8192, K,V ~ 0.5 N(0,1), the MASW
     memory holding the full cache's own raw rows; MASW and full-KV graph steps over the
@@ -606,6 +624,8 @@ def main():
     print(f"[bench] verifier {ver}", file=sys.stderr, flush=True)
     single = single_sequence_leg(dev)
     print(f"[bench] batch-1 prefix-8192 {single}", file=sys.stderr, flush=True)
+    rb = rollback_leg(dev)
+    print(f"[bench] rollback {rb}", file=sys.stderr, flush=True)
     second = None if args.no_sweep else second_workload_leg(dev)
     for row in second or ():
         print(f"[bench] second workload {row}", file=sys.stderr, flush=True)
@@ -631,7 +651,7 @@ def main():
         "hbm_gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(value * sh.batch, 1),
         "fullkv_at_prefix": full_head, "sweep": sweep, "eq3_fit": fits, "device_err_bits": err_bits,
-        "batch1_prefix8192": single, "second_workloads": second, "streaming_read": sread,
+        "batch1_prefix8192": single, "second_workloads": second, "rollback": rb, "streaming_read": sread,
         "materialization": mat, "verifier": ver,
         "roofline": roof, "cpu_baseline": cpu,
     }

@@ -39,6 +39,12 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
       S = 0 it is the pure sliding window [TR] §3 opens with, which is also [TR] §4's SWA
       baseline (1,024-token window).  No slot is ever visible, the ring keeps C = W rows
       and every append is legal.
+* R10 Draft prefill ([TR] §3.3 Algorithm 2 step 2: one pass over the prefix under the
+      structured mask of Appendix C, which the pages do not print, slots materialized in
+      the same pass) computes what decoding the prefix token by token would: the raw
+      query at position i attends to keylist(i), slot g_m's query to keylist(t_m - r)
+      (reading R1); slot K/V depend only on the slots' hidden states, so they are all
+      projected first.
 * R9  Rollback ([TR] §3.3 Algorithm 2 step 6): after the target accepts the first L_acc
       of the draft's candidates, the memory is what appending only the accepted tokens
       would have built: raw tokens past the accepted length t_acc are dropped and so is
@@ -357,6 +363,37 @@ def physical_keylist(t: int, S: int, W: int, r: int) -> List[Tuple[int, int, int
         else:
             out.append((1, ring_cell(idx, S, W, r), idx))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Draft prefill (reading R10)
+# ---------------------------------------------------------------------------
+
+def prefill_attend(raw_k: np.ndarray, raw_v: np.ndarray, slot_k: np.ndarray, slot_v: np.ndarray,
+                   q: np.ndarray, q_slot: np.ndarray, S: int, W: int, r: int,
+                   scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of every prefix query under the decode-time memory of its step.
+
+    raw_k/raw_v [P][Hkv][D] hold positions 1..P; slot_k/slot_v [n][Hkv][D] slots 1..n
+    (n = n(P)); q [P][Hq][D] the raw queries, q_slot [n][Hq][D] the slot queries.
+    Returns out [P][Hq][D] (query at position i over keylist(i)) and o_slot [n][Hq][D]
+    (g_m over keylist(t_m - r)).
+    """
+    def gather(keys):
+        ks = [raw_k[i - 1] if kind == "raw" else slot_k[i - 1] for kind, i in keys]
+        vs = [raw_v[i - 1] if kind == "raw" else slot_v[i - 1] for kind, i in keys]
+        return (np.stack(ks, axis=1).astype(np.float64), np.stack(vs, axis=1).astype(np.float64))
+
+    P, n = q.shape[0], q_slot.shape[0]
+    out = np.zeros(q.shape, np.float64)
+    for i in range(1, P + 1):
+        K, V = gather(keylist(i, S, W, r))
+        out[i - 1] = gqa_attend(np.asarray(q[i - 1], np.float64), K, V, scale)
+    o_slot = np.zeros(q_slot.shape, np.float64)
+    for m in range(1, n + 1):
+        K, V = gather(slot_query_keylist(m, S, W, r))
+        o_slot[m - 1] = gqa_attend(np.asarray(q_slot[m - 1], np.float64), K, V, scale)
+    return out, o_slot
 
 
 # ---------------------------------------------------------------------------

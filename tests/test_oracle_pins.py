@@ -568,3 +568,56 @@ def test_rollback_rows_keep_needed_tokens_resident(S, W, r, R):
     assert _ring_run(S, W, r, R, depth=R)
     assert _ring_run(S, W, r, R, depth=R + 1)
     assert not all(_ring_run(S, W, r, R, depth=R + 2, seed=sd) for sd in range(8))
+
+
+# ---------------------------------------------------------------------------
+# Draft prefill (reading R10, [TR] §3.3 Algorithm 2 step 2)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,W,r", [(2, 8, 4), (0, 5, 2), (4, 16, 8), (3, 6, 0)])
+def test_prefill_equals_token_by_token_decoding(S, W, r):
+    """One pass over the prefix gives exactly what appending and decoding one token at a
+    time (materializing at every boundary) gives: same keys, same order, same fp64 ops."""
+    rng = np.random.default_rng(S + 10 * W + 100 * r)
+    P, Hkv, G, D, hidden = 60, 2, 3, 4, 6
+    raw_k, raw_v = rng.normal(size=(P, Hkv, D)), rng.normal(size=(P, Hkv, D))
+    q = rng.normal(size=(P, Hkv * G, D))
+    n = O.visible_slot_count(P, S, W, r)
+    h = rng.normal(size=(max(n, 1), hidden))
+    wk, wv = rng.normal(size=(hidden, Hkv * D)), rng.normal(size=(hidden, Hkv * D))
+    q_slot = rng.normal(size=(max(n, 1), Hkv * G, D))[:n]
+    # one row at a time, as materialize projects (a batched BLAS product rounds differently)
+    rows = [O.project_slot(h[m], wk, wv, Hkv, D, bf16_cache=False) for m in range(n)]
+    slot_k = np.stack([k for k, _ in rows]) if n else np.zeros((0, Hkv, D))
+    slot_v = np.stack([v for _, v in rows]) if n else np.zeros((0, Hkv, D))
+    scale = 0.37
+    out, o_slot = O.prefill_attend(raw_k, raw_v, slot_k, slot_v, q, q_slot, S, W, r, scale)
+    mem = O.DraftMemory(S, W, r, Hkv, D, bf16_cache=False)
+    for i in range(1, P + 1):
+        mem.append(raw_k[i - 1:i], raw_v[i - 1:i])
+        m = mem.pending_boundary()
+        if m:
+            og = mem.materialize(h[m - 1], wk, wv, q_slot[m - 1], scale)
+            np.testing.assert_array_equal(og, o_slot[m - 1])
+        np.testing.assert_array_equal(mem.decode(q[i - 1], scale), out[i - 1])
+    assert len(mem.slots) == n
+
+
+def test_prefill_dense_mask_bruteforce():
+    """The same prefill from masks over every entry ever created, written separately."""
+    S, W, r, P, D = 2, 6, 3, 40, 5
+    rng = np.random.default_rng(9)
+    raw_k, raw_v = rng.normal(size=(P, 1, D)), rng.normal(size=(P, 1, D))
+    n = O.visible_slot_count(P, S, W, r)
+    slot_k, slot_v = rng.normal(size=(n, 1, D)), rng.normal(size=(n, 1, D))
+    q, q_slot = rng.normal(size=(P, 1, D)), rng.normal(size=(n, 1, D))
+    out, o_slot = O.prefill_attend(raw_k, raw_v, slot_k, slot_v, q, q_slot, S, W, r, 0.5)
+    for i in range(1, P + 1):
+        ref = O.dense_mask_decode(q[i - 1, 0], raw_k[:i, 0], raw_v[:i, 0], slot_k[:, 0], slot_v[:, 0],
+                                  i, S, W, r, 0.5)
+        np.testing.assert_allclose(out[i - 1, 0], ref, atol=1e-12)
+    for m in range(1, n + 1):
+        tm = O.boundary_step(m, S, W, r)
+        ref = O.dense_mask_slot_query(q_slot[m - 1, 0], raw_k[:tm, 0], raw_v[:tm, 0], slot_k[:m, 0],
+                                      slot_v[:m, 0], m, S, W, r, 0.5)
+        np.testing.assert_allclose(o_slot[m - 1, 0], ref, atol=1e-12)

@@ -82,8 +82,6 @@ __device__ __forceinline__ void load_frag(uint32_t (&w)[NW], const T* p) {
   }
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T, int NW>
 __device__ __forceinline__ float frag_dot(const uint32_t (&a)[NW], const uint32_t (&b)[NW]) {
@@ -284,8 +282,6 @@ __device__ __forceinline__ void load_tile(uint32_t (&fk)[U][NW], uint32_t (&fv)[
 // instruction i (K rows, then V rows; chunk-major inside a row) writes 64 lanes x 16
 // bytes at stage + i KB, lane l at byte 16 l, so read_tile_lds hands every lane exactly
 // the fragment load_tile would have loaded.  Completion is tracked by vmcnt only.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 template <typename T, int D, int U, int NW, int CH, int RPI>
 __device__ __forceinline__ void issue_tile_lds(u32x4_t* stage, int tile, int k0, int k1, int lgrp,
                                                const KeySpan& ks, const MemGeom& g, const T* kb0, const T* vb0,
@@ -320,10 +316,6 @@ __device__ __forceinline__ void read_tile_lds(uint32_t (&fk)[U][NW], uint32_t (&
     }
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8; a field at its maximum does not wait).
-constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
-constexpr int kWaitLgkm0 = 0xf | (0x3 << 14) | (0x7 << 4);
 
 // Online-softmax update of (m, l, acc) with one tile.
 template <typename T, int G, int U, int NW, int EPL, int LPR, int RPI>
@@ -368,7 +360,7 @@ __device__ __forceinline__ void reduce_tile(const uint32_t (&fk)[U][NW], const u
       uint32_t pp[G];
 #pragma unroll
       for (int g = 0; g < G; ++g)
-        pp[g] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{s[u][g], s[u + 1][g]}, bf16x2_t));
+        pp[g] = cvt_pk_bf16(s[u][g], s[u + 1][g]);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const uint32_t lo = __builtin_amdgcn_perm(fv[u + 1][w], fv[u][w], 0x05040100u);

@@ -17,6 +17,24 @@ constexpr int kWave = 64;
 // 16 bytes as a native vector (struct types such as uint4 can end up in scratch memory
 // when indexed).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;          // LDS-DMA destination
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;      // LDS transpose-read source
+
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; a field at its maximum does not wait).  The compiler does not order a
+// read of LDS after the asynchronous global->LDS copies that fill it: kernels wait
+// with these explicitly.
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+constexpr int kWaitLgkm0 = 0xf | (0x3 << 14) | (0x7 << 4);
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32 (bf16 = upper half of an IEEE binary32)

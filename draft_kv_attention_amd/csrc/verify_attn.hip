@@ -355,23 +355,10 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyArgs a) {
 //   fetches), so the K-operand reads (32 rows, one chunk each) hit 16 distinct slots.
 // Each wave computes all NB row blocks for its keys; the waves then merge through LDS.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void* vlds_ptr_t;
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t vlds_v4i16_t;
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef float vf32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 vbf16x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(vf32x2_t{lo, hi}, vbf16x2_t));
-}
 constexpr int kVWaveKeys = 32;                        // keys per wave tile
 constexpr int kVStageInstr = 2 * kVWaveKeys * kD * 2 / 1024;   // 16 copies of 1 KB
 constexpr int kVStageU4 = kVStageInstr * kWave;       // 16-byte words per stage
 constexpr int kVSplitRound = kVWaves * kVWaveKeys;    // keys per split rounding unit
-constexpr int vwait_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
-constexpr int kVWaitLgkm0 = 0xf | (0x3 << 14) | (0x7 << 4);
 
 __device__ __forceinline__ void verify_issue(u32x4_t* stage, const uint16_t* kbase, const uint16_t* vbase, int tile,
                                              int k1, int lane) {
@@ -382,9 +369,9 @@ __device__ __forceinline__ void verify_issue(u32x4_t* stage, const uint16_t* kba
     const int key = min(tile + row, k1 - 1);   // rows past the range re-read the last key (masked)
     const int chunk = slot ^ (row & 15);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + size_t(key) * kD + chunk * 8),
-                                     (vlds_ptr_t)(stage + q * kWave), 16, 0, 0);
+                                     (lds_ptr_t)(stage + q * kWave), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + size_t(key) * kD + chunk * 8),
-                                     (vlds_ptr_t)(stage + (kVWaveKeys / 4 + q) * kWave), 16, 0, 0);
+                                     (lds_ptr_t)(stage + (kVWaveKeys / 4 + q) * kWave), 16, 0, 0);
   }
 }
 
@@ -472,8 +459,8 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
   if (nt > 1) verify_issue(vpipe[wave][1], kbase, vbase, w0 + kVWaveKeys, w1, lane);
   int st = 0;
   for (int i = 0; i < nt; ++i) {
-    if (i + 1 < nt) __builtin_amdgcn_s_waitcnt(vwait_vm(kVStageInstr));   // only tile i+1 outstanding
-    else __builtin_amdgcn_s_waitcnt(vwait_vm(0));
+    if (i + 1 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kVStageInstr));   // only tile i+1 outstanding
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     const u32x4_t* stg = vpipe[wave][st];
     const uint16_t* vst = reinterpret_cast<const uint16_t*>(stg + kVStageU4 / 2);
     // K operand (A of S^T): key l32, d = 16 ks + 8 half .. +7
@@ -500,7 +487,7 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
           for (int part = 0; part < 2; ++part) {
             const int key = 16 * step + 4 * hh + 8 * part + (j >> 2);
             const uint16_t* src = vst + key * kD + ((cd ^ (key & 15)) << 3) + e;
-            const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((vlds_v4i16_t*)src);
+            const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
             const u32x2_t y = __builtin_bit_cast(u32x2_t, x);
             w[2 * part] = y.x;
             w[2 * part + 1] = y.y;
@@ -509,7 +496,7 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(kVWaitLgkm0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     const int tile = w0 + i * kVWaveKeys;
     if (i + 2 < nt) verify_issue(vpipe[wave][st], kbase, vbase, tile + 2 * kVWaveKeys, w1, lane);
     st ^= 1;

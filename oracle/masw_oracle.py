@@ -371,13 +371,15 @@ def physical_keylist(t: int, S: int, W: int, r: int) -> List[Tuple[int, int, int
 
 def prefill_attend(raw_k: np.ndarray, raw_v: np.ndarray, slot_k: np.ndarray, slot_v: np.ndarray,
                    q: np.ndarray, q_slot: np.ndarray, S: int, W: int, r: int,
-                   scale: float) -> Tuple[np.ndarray, np.ndarray]:
+                   scale: float, positions: Optional[Sequence[int]] = None,
+                   slots: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention of every prefix query under the decode-time memory of its step.
 
     raw_k/raw_v [P][Hkv][D] hold positions 1..P; slot_k/slot_v [n][Hkv][D] slots 1..n
     (n = n(P)); q [P][Hq][D] the raw queries, q_slot [n][Hq][D] the slot queries.
     Returns out [P][Hq][D] (query at position i over keylist(i)) and o_slot [n][Hq][D]
-    (g_m over keylist(t_m - r)).
+    (g_m over keylist(t_m - r)).  ``positions`` / ``slots`` (1-based) restrict the work
+    to those queries; the other rows are left zero.
     """
     def gather(keys):
         ks = [raw_k[i - 1] if kind == "raw" else slot_k[i - 1] for kind, i in keys]
@@ -386,11 +388,11 @@ def prefill_attend(raw_k: np.ndarray, raw_v: np.ndarray, slot_k: np.ndarray, slo
 
     P, n = q.shape[0], q_slot.shape[0]
     out = np.zeros(q.shape, np.float64)
-    for i in range(1, P + 1):
+    for i in (range(1, P + 1) if positions is None else positions):
         K, V = gather(keylist(i, S, W, r))
         out[i - 1] = gqa_attend(np.asarray(q[i - 1], np.float64), K, V, scale)
     o_slot = np.zeros(q_slot.shape, np.float64)
-    for m in range(1, n + 1):
+    for m in (range(1, n + 1) if slots is None else slots):
         K, V = gather(slot_query_keylist(m, S, W, r))
         o_slot[m - 1] = gqa_attend(np.asarray(q_slot[m - 1], np.float64), K, V, scale)
     return out, o_slot

@@ -17,6 +17,9 @@ Gaussians of the same shapes stand in for them):
 * ``SWEEP_3B``  - the same shapes at B=8, t in {1K,2K,4K,8K,16K,24K,32K}; K,V ~ N(0,1).
 * ``MATERIALIZE_3B`` - slot materialization chain at 3B shapes, B=4, mirrored
                   projections 3072x1024 bf16 ~ N(0, 0.02), H ~ N(0,1), 512 boundaries.
+* ``PREFILL_3B`` - draft prefill at the 3B draft shapes (S=4, W=2048, r=64), B=1, a
+                  32768-token prefix with its 479 slots; K,V,q ~ N(0,1), H ~ N(0,1),
+                  mirrored projections ~ N(0, 0.02).
 * ``VERIFY_8B`` / ``VERIFY_70B`` - verifier attention, 32/64 q heads, 8 KV heads,
                   D=128, bf16, prefix 32768 plus 6 causal query positions, B=4.
 
@@ -70,6 +73,9 @@ SWEEP_PREFIXES = (1024, 2048, 4096, 8192, 16384, 24576, 32768)
 
 MATERIALIZE_3B = dataclasses.replace(DRAFT_3B, name="materialize3b_b4", batch=4, kv_std=1.0)
 MATERIALIZE_CHAIN = 512
+
+PREFILL_3B = dataclasses.replace(DRAFT_3B, name="prefill3b_b1_p32768", batch=1, kv_std=1.0)
+PREFILL_LEN = 32768
 
 
 @dataclasses.dataclass(frozen=True)
@@ -161,6 +167,20 @@ def slot_inputs(shape: DraftShape, seed: int, layer: int, m: int, device="cpu"):
     qg = normal((shape.batch, shape.n_q_heads, shape.head_dim), seed_for(seed, 5, layer, m),
                 std=shape.q_std, dtype=shape.dtype, device=device)
     return h, qg
+
+
+def prefill_inputs(shape: DraftShape, seed: int, layer: int, P: int, ns: int, device="cpu"):
+    """A whole prefix of one layer: raw K/V [B][P][Hkv][D] (row i-1 = position i), raw
+    queries [B][P][Hq][D], slot hidden states [B][ns][hidden] and slot queries
+    [B][ns][Hq][D] (row m-1 = slot m)."""
+    k, v = token_kv(shape, seed, layer, 1, P, device)
+    q = normal((shape.batch, P, shape.n_q_heads, shape.head_dim), seed_for(seed, 6, layer, P),
+               std=shape.q_std, dtype=shape.dtype, device=device)
+    h = normal((shape.batch, ns, shape.hidden), seed_for(seed, 7, layer, ns), std=shape.h_std,
+               dtype=shape.dtype, device=device)
+    qs = normal((shape.batch, ns, shape.n_q_heads, shape.head_dim), seed_for(seed, 8, layer, ns),
+                std=shape.q_std, dtype=shape.dtype, device=device)
+    return k, v, q, h, qs
 
 
 def full_cache(batch: int, n_kv_heads: int, max_len: int, head_dim: int, seed: int,

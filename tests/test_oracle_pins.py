@@ -621,3 +621,22 @@ def test_prefill_dense_mask_bruteforce():
         ref = O.dense_mask_slot_query(q_slot[m - 1, 0], raw_k[:tm, 0], raw_v[:tm, 0], slot_k[:m, 0],
                                       slot_v[:m, 0], m, S, W, r, 0.5)
         np.testing.assert_allclose(o_slot[m - 1, 0], ref, atol=1e-12)
+
+
+def test_prefill_subset_rows_equal_the_full_pass():
+    """Restricting the prefill to some queries gives those rows of the full pass exactly
+    and leaves the others zero (the GPU tests sample rows at full size this way)."""
+    S, W, r, P, D = 2, 6, 3, 40, 5
+    rng = np.random.default_rng(11)
+    raw_k, raw_v = rng.normal(size=(P, 2, D)), rng.normal(size=(P, 2, D))
+    n = O.visible_slot_count(P, S, W, r)
+    slot_k, slot_v = rng.normal(size=(n, 2, D)), rng.normal(size=(n, 2, D))
+    q, q_slot = rng.normal(size=(P, 4, D)), rng.normal(size=(n, 4, D))
+    full, full_s = O.prefill_attend(raw_k, raw_v, slot_k, slot_v, q, q_slot, S, W, r, 0.5)
+    pos, sl = [1, 7, 9, 40], [2, n]
+    part, part_s = O.prefill_attend(raw_k, raw_v, slot_k, slot_v, q, q_slot, S, W, r, 0.5,
+                                    positions=pos, slots=sl)
+    for i in range(1, P + 1):
+        np.testing.assert_array_equal(part[i - 1], full[i - 1] if i in pos else 0.0)
+    for m in range(1, n + 1):
+        np.testing.assert_array_equal(part_s[m - 1], full_s[m - 1] if m in sl else 0.0)

@@ -84,6 +84,8 @@ _SIGS = {
     "masw_debug_keylist": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P]),
     "masw_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_int32, _P, _P]),
     "masw_rollback": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "masw_prefill": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
+                                    ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -397,6 +399,42 @@ def masw_rollback(d: Dims, layer: Layer, seq: Seq, t_spec: torch.Tensor, stream=
     dc, lc, sc = d.c(), layer.c(), seq.c()
     _ok("masw_rollback", lib().masw_rollback(ctypes.byref(dc), ctypes.byref(lc), ctypes.byref(sc),
                                              t_spec.data_ptr(), _stream(stream)))
+
+
+def masw_prefill(d: Dims, layer: Layer, seq: Seq, k: torch.Tensor, v: torch.Tensor,
+                 q: torch.Tensor, out: torch.Tensor, h_slot: Optional[torch.Tensor] = None,
+                 w_k_g: Optional[torch.Tensor] = None, w_v_g: Optional[torch.Tensor] = None,
+                 q_slot: Optional[torch.Tensor] = None, o_slot: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    """Draft prefill of P = seq.seq_len[b] tokens per sequence (see include/masw.h):
+    k, v [B][p_max][Hkv][D], q, out [B][p_max][Hq][D]; with a slot chain also h_slot
+    [B][ns_max][hidden], w_k_g, w_v_g [hidden][Hkv*D], q_slot, o_slot [B][ns_max][Hq][D]."""
+    _check_layer(d, layer)
+    _check_seq(d, seq)
+    p_max = k.shape[1]
+    for nm, t in (("k", k), ("v", v)):
+        _check(t, nm, (d.batch, p_max, d.n_kv_heads, d.head_dim), d.dtype)
+    for nm, t in (("q", q), ("out", out)):
+        _check(t, nm, (d.batch, p_max, d.n_q_heads, d.head_dim), d.dtype)
+    ns_max, hidden = 0, 0
+    ptrs = [None] * 5
+    if h_slot is not None:
+        ns_max, hidden = h_slot.shape[1], h_slot.shape[2]
+        _check(h_slot, "h_slot", (d.batch, ns_max, hidden), d.dtype)
+        for nm, t in (("w_k_g", w_k_g), ("w_v_g", w_v_g)):
+            if t is None:
+                raise ValueError(f"{nm} is required with h_slot")
+            _check(t, nm, (hidden, d.n_kv_heads * d.head_dim), d.dtype)
+        for nm, t in (("q_slot", q_slot), ("o_slot", o_slot)):
+            if t is None:
+                raise ValueError(f"{nm} is required with h_slot")
+            _check(t, nm, (d.batch, ns_max, d.n_q_heads, d.head_dim), d.dtype)
+        ptrs = [h_slot.data_ptr(), w_k_g.data_ptr(), w_v_g.data_ptr(), q_slot.data_ptr(),
+                o_slot.data_ptr()]
+    dc, lc, sc = d.c(), layer.c(), seq.c()
+    _ok("masw_prefill", lib().masw_prefill(
+        ctypes.byref(dc), ctypes.byref(lc), ctypes.byref(sc), p_max, k.data_ptr(), v.data_ptr(),
+        q.data_ptr(), out.data_ptr(), ns_max, hidden, *ptrs, _stream(stream)))
 
 
 def stream_read(buf: torch.Tensor, sums: torch.Tensor, work_groups: int = 0, stream=None) -> None:

@@ -7,7 +7,8 @@
 // evicts the token i-(W+r), which is legal only once that token's block has its slot.
 // Each thread moves one 16-byte packet of K and of V; all packets of one token take
 // the same decision (append_fate), so an illegal token is skipped whole, and so is a
-// token a later position of the same call overwrites.
+// token a later position of the same call overwrites.  A prefill append takes a whole
+// prefix per sequence and moves only the tokens the memory keeps after it.
 #include "masw_internal.hpp"
 
 namespace masw {
@@ -18,12 +19,22 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   constexpr int VEC = 16 / int(sizeof(T));
   const int b = blockIdx.y;
   const int per_tok = a.Hkv * a.D;
-  const int packets = a.n_new * per_tok / VEC;
+  const bool prefill = a.prefill_len > 0;
+  // prefill: token slots [0, S) are the sinks, [S, S + C) the newest C positions
+  const int n_tok = prefill ? a.g.S + a.g.C : a.n_new;
+  const int packets = n_tok * per_tok / VEC;
   const int t = a.seq_len[b];
-  if (t < a.n_new || (a.max_len > 0 && t > a.max_len)) {
+  if (prefill ? (t < 0 || t > a.prefill_len) : (t < a.n_new || (a.max_len > 0 && t > a.max_len))) {
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SEQ_RANGE);
     return;
   }
+  if (prefill && a.g.r > 0) {
+    // the prefill's projection publishes n_slots = n(t); if it could not (it reported
+    // why), the sequence is left alone
+    const int dd = t - a.g.S - a.g.W;
+    if (a.n_slots[b] != (dd > 0 ? dd / a.g.r : 0)) return;
+  }
+  const int first = prefill ? max(a.g.S, t - a.g.C) + 1 : 0;   // oldest ring position a prefill keeps
   int bits = 0;
   for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < packets; p += gridDim.x * blockDim.x) {
     const int e = p * VEC;
@@ -31,7 +42,15 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     const int rem = e - j * per_tok;
     const int kvh = rem / a.D;
     const int d = rem - kvh * a.D;
-    const int i = t - a.n_new + 1 + j;
+    int i, src_row;
+    if (prefill) {
+      i = j < a.g.S ? j + 1 : first + (j - a.g.S);
+      if (i > t) continue;
+      src_row = i - 1;
+    } else {
+      i = t - a.n_new + 1 + j;
+      src_row = j;
+    }
     const size_t unit = size_t(b) * a.Hkv + kvh;
     T* dk;
     T* dv;
@@ -48,7 +67,8 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
       dk = static_cast<T*>(a.k_ring);
       dv = static_cast<T*>(a.v_ring);
     }
-    const size_t src = ((size_t(b) * a.n_new + j) * a.Hkv + kvh) * a.D + d;
+    const int src_len = prefill ? a.prefill_len : a.n_new;
+    const size_t src = ((size_t(b) * src_len + src_row) * a.Hkv + kvh) * a.D + d;
     *reinterpret_cast<uint4*>(dk + off) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_new) + src);
     *reinterpret_cast<uint4*>(dv + off) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_new) + src);
   }
@@ -84,7 +104,8 @@ int launch_rollback(const MemGeom& g, int rollback, const int32_t* seq_len, cons
 
 int launch_append(const AppendArgs& a, int dtype, hipStream_t s) {
   const int vec = dtype == MASW_BF16 ? 8 : 4;
-  const long packets = long(a.n_new) * a.Hkv * a.D / vec;
+  const long tokens = a.prefill_len > 0 ? long(a.g.S) + a.g.C : long(a.n_new);
+  const long packets = tokens * a.Hkv * a.D / vec;
   const int blocks = int(std::min<long>((packets + 255) / 256, 1024));
   if (dtype == MASW_BF16)
     hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(blocks, a.B), dim3(256), 0, s, a);

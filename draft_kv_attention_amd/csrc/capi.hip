@@ -349,6 +349,89 @@ MASW_API int masw_rollback(const masw_dims* d, const masw_layer* L, const masw_s
   return launch_rollback(masw_geom(d), d->rollback, seq->seq_len, t_spec, L->n_slots, seq->err, d->batch, stream);
 }
 
+MASW_API int masw_prefill(const masw_dims* d, const masw_layer* L, const masw_seq* seq, int32_t p_max,
+                          const void* k, const void* v, const void* q, void* out, int32_t ns_max, int32_t hidden,
+                          const void* h_slot, const void* w_k_g, const void* w_v_g, const void* q_slot,
+                          void* o_slot, hipStream_t stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if ((st = check_layer(d, L))) return st;
+  if (!seq || !seq->seq_len || !seq->err || !k || !v || !q || !out || p_max < 1 || ns_max < 0) return MASW_ERR_ARG;
+  if (d->dtype != MASW_BF16 || d->head_dim != 128) return MASW_ERR_UNIMPLEMENTED;
+  const bool slots = d->interval > 0 && ns_max > 0;
+  if (slots && (!h_slot || !w_k_g || !w_v_g || !q_slot || !o_slot || hidden < 1)) return MASW_ERR_ARG;
+  if (slots && hidden % 8) return MASW_ERR_SHAPE;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  const int qb = prefill_rows_per_block() / G;
+  const long raw_blocks = (long(p_max) + qb - 1) / qb, slot_blocks = slots ? (long(ns_max) + qb - 1) / qb : 0;
+  const long groups = slots ? (long(d->batch) * ns_max + 15) / 16 : 0;
+  if ((raw_blocks + slot_blocks) * d->n_kv_heads * d->batch > 0x7fffffffL || groups > 65535) return MASW_ERR_SHAPE;
+
+  // 1. every slot of the prefix (Algorithm 1 step 3, all boundaries at once); n_slots = n(P)
+  if (slots) {
+    ProjectArgs pa{};
+    pa.h = h_slot;
+    pa.w_k = w_k_g;
+    pa.w_v = w_v_g;
+    pa.k_slot = L->k_slot;
+    pa.v_slot = L->v_slot;
+    pa.seq_len = seq->seq_len;
+    pa.n_slots = L->n_slots;
+    pa.err = seq->err;
+    pa.g = masw_geom(d);
+    pa.B = d->batch;
+    pa.Hkv = d->n_kv_heads;
+    pa.D = d->head_dim;
+    pa.hidden = hidden;
+    pa.ksplits = 1;
+    pa.k_per_split = (hidden + 127) / 128 * 128;
+    pa.prefill_ns = ns_max;
+    if ((st = launch_project(pa, d->dtype, stream))) return st;
+  }
+  // 2. the raw tokens the memory keeps after the prefix (sinks and the newest C)
+  AppendArgs aa{};
+  aa.k_sink = L->k_sink ? L->k_sink : L->k_ring;
+  aa.v_sink = L->v_sink ? L->v_sink : L->v_ring;
+  aa.k_ring = L->k_ring;
+  aa.v_ring = L->v_ring;
+  aa.sink_cap = d->sink;
+  aa.g = masw_geom(d);
+  aa.seq_len = seq->seq_len;
+  aa.err = seq->err;
+  aa.n_slots = L->n_slots;
+  aa.k_new = k;
+  aa.v_new = v;
+  aa.B = d->batch;
+  aa.Hkv = d->n_kv_heads;
+  aa.D = d->head_dim;
+  aa.prefill_len = p_max;
+  if ((st = launch_append(aa, d->dtype, stream))) return st;
+  // 3. every raw query and slot query under the memory of its own step
+  PrefillArgs a{};
+  a.k = k;
+  a.v = v;
+  a.k_slot = or_else(L->k_slot, L->k_ring);
+  a.v_slot = or_else(L->v_slot, L->v_ring);
+  a.n_slots = L->n_slots;
+  a.g = masw_geom(d);
+  a.seq_len = seq->seq_len;
+  a.err = seq->err;
+  a.q = q;
+  a.q_slot = q_slot;
+  a.out = out;
+  a.o_slot = o_slot;
+  a.B = d->batch;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.p_max = p_max;
+  a.ns_max = slots ? ns_max : 0;
+  a.qb = qb;
+  a.raw_blocks = int(raw_blocks);
+  a.slot_blocks = int(slot_blocks);
+  a.scale_log2 = scale_log2(d);
+  return launch_prefill(a, stream);
+}
+
 MASW_API int fullkv_verify_attn(const masw_dims* d, const void* k, const void* v, int32_t max_len,
                                 const int32_t* seq_len, int32_t* err, int32_t n_q, const void* q, void* out,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {

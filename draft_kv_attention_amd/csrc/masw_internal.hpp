@@ -116,6 +116,10 @@ struct AppendArgs {
   int max_len;              // full cache bound (0: none)
   const void* k_new; const void* v_new;   // [B][n_new][Hkv][D]
   int B, Hkv, D, n_new;
+  // Prefill (> 0): k_new/v_new hold a whole prefix [B][prefill_len][Hkv][D], each
+  // sequence appends its own seq_len[b] positions, and only the ones the memory keeps
+  // (sinks and the newest C) are moved; n_new is unused.
+  int prefill_len;
 };
 
 int launch_append(const AppendArgs& a, int dtype, hipStream_t s);
@@ -132,7 +136,7 @@ struct ProjectArgs {
   const void* w_k; const void* w_v;   // [hidden][Hkv*D]
   void* k_slot; void* v_slot;         // [B][Hkv][max_slots][D]
   const int32_t* seq_len;
-  const int32_t* n_slots;
+  int32_t* n_slots;         // read at a boundary; written by a prefill
   int32_t* err;
   int32_t* active;          // [B] workspace
   MemGeom g;
@@ -144,6 +148,11 @@ struct ProjectArgs {
   int ksplits, k_per_split;
   float* part;
   int32_t* counters;
+  // Prefill (> 0): h holds prefill_ns slot hidden states per sequence
+  // ([B][prefill_ns][hidden]); rows are (sequence, slot) pairs and every slot
+  // 1..n(seq_len[b]) is projected, after which n_slots[b] = n(seq_len[b]).  Needs
+  // ksplits == 1; `active` is not used.
+  int prefill_ns;
 };
 
 constexpr int kMaxProjectSplits = 8;
@@ -158,6 +167,29 @@ inline int project_splits(int hidden) {
 }
 
 int launch_project(const ProjectArgs& a, int dtype, hipStream_t s);
+
+// Draft prefill attention (bf16, D = 128): every raw query of a prefix and every slot
+// query, each under the memory of its own step.  One work-group per block of `qb`
+// consecutive queries of one (sequence, KV head); blocks [0, raw_blocks) hold raw
+// queries, [raw_blocks, raw_blocks + slot_blocks) slot queries.
+struct PrefillArgs {
+  const void* k; const void* v;             // raw prefix [B][p_max][Hkv][D]
+  const void* k_slot; const void* v_slot;   // the layer's slots [B][Hkv][max_slots][D]
+  const int32_t* n_slots;
+  MemGeom g;
+  const int32_t* seq_len;
+  int32_t* err;
+  const void* q;                            // [B][p_max][Hq][D]
+  const void* q_slot;                       // [B][ns_max][Hq][D]
+  void* out;                                // like q
+  void* o_slot;                             // like q_slot
+  int B, Hq, Hkv, p_max, ns_max;
+  int qb, raw_blocks, slot_blocks;
+  float scale_log2;
+};
+
+int prefill_rows_per_block();
+int launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 // Multi-query verifier attention over a full cache on the matrix cores (bf16, D=128,
 // Hq/Hkv * n_q <= 64 rows per KV head).  Same partial/merge protocol as DecodeArgs.

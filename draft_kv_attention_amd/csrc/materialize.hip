@@ -26,6 +26,22 @@ __device__ __forceinline__ int boundary_slot(const ProjectArgs& a, int b, int& b
   return m;
 }
 
+// Prefill mode: slot index (1-based) of H row `row` = (b, slot row), or 0 if that slot
+// does not exist at t = seq_len[b].  The row of slot 1 also publishes n_slots[b] = n(t).
+__device__ __forceinline__ int prefill_slot(const ProjectArgs& a, int row, bool publish, int& b, int& bits) {
+  b = row / a.prefill_ns;
+  const int mi = row - b * a.prefill_ns;
+  const int t = a.seq_len[b];
+  const int d = t - a.g.S - a.g.W;
+  const int n = d > 0 && a.g.r > 0 ? d / a.g.r : 0;
+  if (n > a.g.max_slots || n > a.prefill_ns) {
+    if (mi == 0) bits |= MASW_DEV_SLOT_CAPACITY;
+    return 0;
+  }
+  if (publish && mi == 0) a.n_slots[b] = n;   // nothing in this launch reads n_slots
+  return mi < n ? mi + 1 : 0;
+}
+
 constexpr int kCols = 64;          // output columns per work-group
 constexpr int kPWaves = 4;
 constexpr int kStepK = 32;         // hidden rows per MFMA step
@@ -47,7 +63,8 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// grid = (N / 64 column blocks, 2 matrices, ksplits x groups of 16 sequences).  A
+// grid = (N / 64 column blocks, 2 matrices, ksplits x groups of 16 rows of H: the
+// sequences at a boundary, or the (sequence, slot) pairs of a prefill).  A
 // work-group reduces hidden rows [ks * k_per_split, +k_per_split) of its 64 columns;
 // each of its 4 waves takes a contiguous quarter, keeps kPF steps of weight loads in
 // flight, transposes each [32 k][64 n] tile through its own LDS tile and feeds four
@@ -61,23 +78,28 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
   const int N = a.Hkv * a.D;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
-  __shared__ int sm_m[16];
+  __shared__ int sm_m[16], sm_b[16];
   __shared__ int sm_any, sm_last;
   __shared__ __attribute__((aligned(16))) float red[kPWaves * 16 * kCols];
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kPWaves * kCols * kTRow];
 
+  // rows of H: sequences, or (sequence, slot) pairs in prefill mode
+  const int rows = a.prefill_ns > 0 ? a.B * a.prefill_ns : a.B;
   if (tid == 0) sm_any = 0;
   __syncthreads();
   if (tid < 16) {
-    const int b = bg * 16 + tid;
-    int bits = 0, m = 0;
-    if (b < a.B) m = boundary_slot(a, b, bits);
-    sm_m[tid] = m;
-    if (m) atomicOr(&sm_any, 1);
-    if (nblk == 0 && which == 0 && ks == 0 && b < a.B) {
-      a.active[b] = m;
-      if (bits) atomicOr(a.err, bits);
+    const int row = bg * 16 + tid;
+    int bits = 0, m = 0, b = row;
+    if (a.prefill_ns > 0) {
+      if (row < rows) m = prefill_slot(a, row, nblk == 0 && which == 0 && ks == 0, b, bits);
+    } else if (row < a.B) {
+      m = boundary_slot(a, b, bits);
+      if (nblk == 0 && which == 0 && ks == 0) a.active[b] = m;
     }
+    sm_m[tid] = m;
+    sm_b[tid] = b;
+    if (m) atomicOr(&sm_any, 1);
+    if (nblk == 0 && which == 0 && ks == 0 && bits) atomicOr(a.err, bits);
   }
   __syncthreads();
   if (!sm_any) return;
@@ -110,7 +132,7 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
                        : u32x4_t{0, 0, 0, 0};
       }
       const int ka = kk + (lane >> 4) * 8;
-      av[p] = on && brow < a.B && ka < a.hidden
+      av[p] = on && brow < rows && ka < a.hidden
                   ? *reinterpret_cast<const u32x4_t*>(H + size_t(brow) * a.hidden + ka)
                   : u32x4_t{0, 0, 0, 0};
     }
@@ -181,9 +203,9 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
   for (int j = 0; j < kOut; ++j) {
     const int idx = tid + j * kPWaves * kWave;
     const int row = idx / kCols, col = idx % kCols;
-    const int b = bg * 16 + row;
+    const int b = sm_b[row];
     const int m = sm_m[row];
-    if (b < a.B && m > 0) {
+    if (m > 0) {
       const int n = nblk * kCols + col;
       const int kvh = n / a.D, d = n - (n / a.D) * a.D;
       dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = f32_to_bf16(s[j]);
@@ -220,9 +242,12 @@ int launch_project(const ProjectArgs& a, int dtype, hipStream_t s) {
   const int N = a.Hkv * a.D;
   if (dtype == MASW_BF16) {
     if (a.ksplits < 1 || a.ksplits > kMaxProjectSplits || a.k_per_split % (kPWaves * kStepK)) return MASW_ERR_ARG;
-    hipLaunchKernelGGL(project_mfma_kernel, dim3(N / kCols, 2, a.ksplits * ((a.B + 15) / 16)),
+    const long rows = a.prefill_ns > 0 ? long(a.B) * a.prefill_ns : long(a.B);
+    if (a.prefill_ns > 0 && a.ksplits != 1) return MASW_ERR_ARG;
+    hipLaunchKernelGGL(project_mfma_kernel, dim3(N / kCols, 2, a.ksplits * ((rows + 15) / 16)),
                        dim3(kPWaves * kWave), 0, s, a);
   } else {
+    if (a.prefill_ns > 0) return MASW_ERR_UNIMPLEMENTED;
     hipLaunchKernelGGL(project_valu_kernel<float>, dim3((2 * N + 255) / 256, a.B), dim3(256), 0, s, a);
   }
   return hipGetLastError() == hipSuccess ? MASW_OK : MASW_ERR_LAUNCH;

@@ -50,7 +50,7 @@ extern "C" {
 #endif
 
 #define MASW_API __attribute__((visibility("default")))
-#define MASW_ABI_VERSION 3
+#define MASW_ABI_VERSION 4
 
 /* ---- host status codes ------------------------------------------------------- */
 enum {
@@ -198,6 +198,33 @@ MASW_API int masw_decode_step(const masw_dims* dims, const masw_layer* layer, co
  * t_spec [B] int32, device.  Call once per layer. */
 MASW_API int masw_rollback(const masw_dims* dims, const masw_layer* layer, const masw_seq* seq,
                            const int32_t* t_spec, hipStream_t stream);
+
+/* Draft prefill ([TR] §3.3 Algorithm 2 step 2): the draft processes a whole prefix of
+ * P = seq_len[b] tokens per sequence in one call.  The structured prefill mask of the
+ * review's Appendix C is not printed; this call computes what decoding the prefix one
+ * token at a time would (materializing each slot at its boundary):
+ *   1. (r > 0 and ns_max > 0) every slot g_1 .. g_n, n = n(P), is projected as in
+ *      masw_materialize_slot step 1 from h_slot [B][ns_max][hidden] (row m-1 holds the
+ *      hidden state of g_m) into slot rows 0 .. n-1, and n_slots[b] = n;
+ *   2. the raw tokens the memory keeps after position P (sinks 1..min(S,P) and the
+ *      newest C ring positions) are copied from k, v [B][p_max][Hkv][D] (row i-1 holds
+ *      position i) into the layer, as masw_evict_append of positions 1..P would leave
+ *      them;
+ *   3. out[b][i-1] [B][p_max][Hq][D] = attention of q[b][i-1] over keylist(i) for every
+ *      i = 1..P (Eq. 2 over Eq. 4), and o_slot[b][m-1] [B][ns_max][Hq][D] = attention of
+ *      the slot query q_slot[b][m-1] over keylist(t_m - r) for m = 1..n (Algorithm 1
+ *      step 2, include_self = 0).  Rows past P (past n) are untouched.
+ * Keys are read from k, v and the projected slots, so the result does not depend on the
+ * layer's earlier contents; the layer must start empty for r > 0 when no slots are
+ * projected (n_slots[b] = 0).  bf16 with D = 128 only (else MASW_ERR_UNIMPLEMENTED);
+ * hidden % 8 == 0.  Device errors: P < 0 or P > p_max: MASW_DEV_SEQ_RANGE;
+ * n(P) > max_slots or > ns_max: MASW_DEV_SLOT_CAPACITY; that sequence's outputs and
+ * memory are left alone.  P = 0 is a no-op for that sequence.  With r = 0 or
+ * ns_max = 0, h_slot, w_k_g, w_v_g, q_slot and o_slot may be NULL.  No workspace. */
+MASW_API int masw_prefill(const masw_dims* dims, const masw_layer* layer, const masw_seq* seq,
+                          int32_t p_max, const void* k, const void* v, const void* q, void* out,
+                          int32_t ns_max, int32_t hidden, const void* h_slot, const void* w_k_g,
+                          const void* w_v_g, const void* q_slot, void* o_slot, hipStream_t stream);
 
 /* Full-KV draft decode attention, the baseline ([TR] §2.3 Eq. 2 over K_{<=t}).
  * k, v [B][Hkv][max_len][D] (row i-1 holds position i); q, out [B][Hq][D]; keys 1..t.

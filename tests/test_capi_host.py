@@ -107,6 +107,26 @@ def test_rollback_rejects_bad_arguments_on_host(lib):
     assert lib.masw_rollback(ctypes.byref(bad), ctypes.byref(layer), ctypes.byref(seq), 1 << 20, None) == -1
 
 
+def test_prefill_rejects_bad_arguments_on_host(lib):
+    layer = M._Layer(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    seq = M._Seq(1 << 20, 1 << 20)
+    P = 1 << 20
+
+    def call(d, p_max=100, k=P, ns_max=4, hidden=3072, h=P, lay=layer):
+        return lib.masw_prefill(ctypes.byref(d), ctypes.byref(lay) if lay else None, ctypes.byref(seq), p_max,
+                                k, P, P, P, ns_max, hidden, h, P, P, P, P, None)
+    d = _dims()
+    assert call(d, p_max=0) == -1
+    assert call(d, k=None) == -1
+    assert call(d, ns_max=-1) == -1
+    assert call(d, h=None) == -1               # a slot chain needs the slot inputs
+    assert call(d, hidden=3071) == -3          # hidden % 8
+    assert call(d, lay=None) == -1
+    assert call(_dims(dtype=M.F32)) == -6      # matrix-core path only
+    assert call(_dims(head_dim=64)) == -6
+    assert call(_dims(interval=2049)) == -1
+
+
 def test_workspace_sizes(lib):
     d = _dims(batch=8)
     a = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_DRAFT_ATTN, 0, 0)

@@ -45,6 +45,7 @@ METRIC = "draft attn steps/s + HBM GB/s (% peak) vs prefix 1K-32K, MASW vs full-
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_b8_prefix32768_hbm_traffic.md")
 DECODE_SOURCES = ("decode_attn.hip", "masw_internal.hpp", "masw_device.hpp")
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak (no sparsity)
 SHAPE = SI.SWEEP_3B
 T_HEAD = 32768
 
@@ -343,6 +344,68 @@ def single_sequence_leg(dev, steps=64, warmup=10):
     return out
 
 
+def prefill_flops(P, S, W, r, Hq, D, hidden=0, n_kv=0):
+    """Algorithmic flops of a prefill: 4 D Hq per (query, visible key) for S = QK^T and
+    O = PV, over every raw query i (keylist(i)) and slot query m (keylist(t_m - r)), plus
+    2 x 2 hidden (Hkv D) per projected slot."""
+    att = sum(keys_at(i, S, W, r) for i in range(1, P + 1))
+    n = n_slots_at(P, S, W, r)
+    att += sum(keys_at(S + W + (m - 1) * r, S, W, r) for m in range(1, n + 1))
+    return 4 * D * Hq * att + 4 * hidden * n_kv * D * n
+
+
+def prefill_leg(dev, reps=10):
+    """Draft prefill of one layer at the 3B draft shape, B = 1, a 32768-token prefix
+    (479 slots): masw_prefill (slot projection, memory load, attention of every raw and
+    slot query), and the same attention kernel as a full causal prefill (every token a
+    sink).  Matrix-core roofline: algorithmic flops / time vs the dense bf16 peak."""
+    sh, P = SI.PREFILL_3B, SI.PREFILL_LEN
+    S, W, r = sh.sink, sh.window, sh.interval
+    n = n_slots_at(P, S, W, r)
+    k, v, q, h, qs = SI.prefill_inputs(sh, 17, 0, P, n, device=dev)
+    wk, wv = SI.mirrored_weights(sh, 17, device=dev)
+    out = torch.empty_like(q)
+    o_slot = torch.empty_like(qs)
+    seq = M.alloc_seq(1, dev)
+    seq.seq_len.fill_(P)
+    res = dict(workload="draft prefill, 3B draft shapes, batch 1, prefix 32768, one layer", prefix=P, slots=n)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    d = M.Dims(batch=1, n_q_heads=sh.n_q_heads, n_kv_heads=sh.n_kv_heads, head_dim=sh.head_dim, sink=S,
+               window=W, interval=r, max_slots=n, dtype=sh.dtype)
+    layer = M.alloc_layer(d, dev, fill=None)
+    layer.n_slots.zero_()
+    ms = timed(lambda: M.masw_prefill(d, layer, seq, k, v, q, out, h, wk, wv, qs, o_slot))
+    fl = prefill_flops(P, S, W, r, sh.n_q_heads, sh.head_dim, sh.hidden, sh.n_kv_heads)
+    res.update(masw_ms=round(ms, 4), masw_tokens_per_s=round(P / (ms * 1e-3), 1),
+               masw_tflops=round(fl / (ms * 1e-3) / 1e12, 1),
+               masw_pct_bf16_peak=round(100 * fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1))
+    # the same kernels as a full causal prefill: S = P, no window beyond it, no slots
+    dfull = M.Dims(batch=1, n_q_heads=sh.n_q_heads, n_kv_heads=sh.n_kv_heads, head_dim=sh.head_dim, sink=P,
+                   window=1, interval=0, max_slots=0, dtype=sh.dtype)
+    lfull = M.alloc_layer(dfull, dev, fill=None)
+    lfull.n_slots.zero_()
+    msf = timed(lambda: M.masw_prefill(dfull, lfull, seq, k, v, q, out))
+    flf = 4 * sh.head_dim * sh.n_q_heads * P * (P + 1) // 2
+    res.update(full_causal_ms=round(msf, 4), full_causal_tflops=round(flf / (msf * 1e-3) / 1e12, 1),
+               full_causal_pct_bf16_peak=round(100 * flf / (msf * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
+               full_over_masw=round(msf / ms, 2), algorithmic_flops_masw=fl, algorithmic_flops_full=flf,
+               device_err_bits=int(seq.err.item()))
+    del layer, lfull
+    torch.cuda.empty_cache()
+    return res
+
+
 def graph_per_call_us(fn, calls, replays=5):
     """Average duration of one call inside a captured graph of `calls` back-to-back calls."""
     s = torch.cuda.Stream()
@@ -562,6 +625,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel roofline leg (for rocprofv3 --kernel-trace --stats)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the draft prefill leg (for rocprofv3 --kernel-trace --stats)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="eager launches of the dominant kernel and a 256 MiB copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -574,6 +639,9 @@ def main():
     sh = SHAPE
     if args.roofline_only or args.traffic_probe:
         profile_modes(args, dev)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_leg(dev)}), flush=True)
         return
     t_max = T_HEAD + args.warmup + args.steps + 8
     if not args.no_sweep:
@@ -626,6 +694,8 @@ def main():
     print(f"[bench] batch-1 prefix-8192 {single}", file=sys.stderr, flush=True)
     rb = rollback_leg(dev)
     print(f"[bench] rollback {rb}", file=sys.stderr, flush=True)
+    pre = prefill_leg(dev)
+    print(f"[bench] prefill {pre}", file=sys.stderr, flush=True)
     second = None if args.no_sweep else second_workload_leg(dev)
     for row in second or ():
         print(f"[bench] second workload {row}", file=sys.stderr, flush=True)
@@ -651,7 +721,7 @@ def main():
         "hbm_gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(value * sh.batch, 1),
         "fullkv_at_prefix": full_head, "sweep": sweep, "eq3_fit": fits, "device_err_bits": err_bits,
-        "batch1_prefix8192": single, "second_workloads": second, "rollback": rb, "streaming_read": sread,
+        "batch1_prefix8192": single, "second_workloads": second, "rollback": rb, "prefill": pre, "streaming_read": sread,
         "materialization": mat, "verifier": ver,
         "roofline": roof, "cpu_baseline": cpu,
     }

@@ -6,15 +6,21 @@
 // at position i has t_q = i, slot g_m's query t_q = t_m - r (§3.2 Algorithm 1 step 2).
 //
 // Work-group = one block of QB consecutive queries (raw positions, or slot indices) of
-// one (sequence, KV head): R = QB * G rows (query-major: row = qi * G + g), in NB = 2
-// row blocks of 32.  Its key list is sinks ++ the raw band
-// [max(S, t_first - W), t_last) ++ slots [0, n(t_last)), each row masked to its own
-// keylist(t_q).  The 4 waves stream contiguous quarters of that list through private
-// LDS stages filled by asynchronous global->LDS copies (same tile format as the
-// verifier: 32 keys, rows swizzled by 16-byte slot), and compute on the matrix cores:
+// one (sequence, KV head): R = QB * G <= 256 rows (query-major: row = qi * G + g).  Its
+// key list is sinks ++ the raw band [max(S, t_first - W), t_last) ++ slots
+// [0, n(t_last)), each row masked to its own keylist(t_q).
+//
+// The four waves own 64 rows each (Q in registers) and walk the key list together in
+// 32-key tiles.  The work-group streams the tiles through a ring of LDS stages with
+// asynchronous global->LDS copies (K rows then V rows, each row's 16-byte slots
+// XOR-swizzled by the row index), one barrier per tile; each wave computes on the
+// matrix cores
 //   S^T[key][row] = K[key][d] . Q^T[d][row]      (v_mfma_f32_32x32x16_bf16)
 //   O^T[d][row]  += V^T[d][key] . P^T[key][row]  (V^T via ds_read_b64_tr_b16)
-// then merge through LDS in wave order and write out / o_slot (bf16).
+// with an online softmax whose reference max is only raised when a row's scores exceed
+// it by more than 2^8 (the rescale of the accumulators is then rare; the result is the
+// same softmax), skipping tiles none of its rows can see and masking only tiles that
+// not all of its rows see whole.
 #include "masw_internal.hpp"
 
 namespace masw {
@@ -23,16 +29,21 @@ namespace {
 constexpr int kPWaves = 4;
 constexpr int kPThreads = kPWaves * kWave;
 constexpr int kPD = 128;
-#ifndef MASW_PREFILL_NB
-#define MASW_PREFILL_NB 2
+constexpr int kPNB = 2;                               // row blocks of 32 per wave
+constexpr int kPWaveRows = kPNB * 32;
+constexpr int kPRows = kPWaves * kPWaveRows;          // rows per work-group
+constexpr int kPTile = 32;                            // keys per stage
+#ifndef MASW_PREFILL_STAGES
+#define MASW_PREFILL_STAGES 6
 #endif
-constexpr int kPNB = MASW_PREFILL_NB;        // row blocks per work-group
-constexpr int kPRows = kPNB * 32;
-constexpr int kPRS = 136;                    // padded LDS row of Q (bf16 elements)
-constexpr int kPTile = 32;                   // keys per wave tile
-constexpr int kPStageInstr = 2 * kPTile * kPD * 2 / 1024;   // 16 copies of 1 KB
-constexpr int kPStageU4 = kPStageInstr * kWave;
-constexpr int kAccRow = kPD + 4;             // merge buffer row (fp32), padded
+constexpr int kPStages = MASW_PREFILL_STAGES;
+constexpr int kPStageU4 = 2 * kPTile * kPD * 2 / 16;  // 16-byte words per stage (K then V)
+constexpr int kPIssue = kPStageU4 / kPThreads;        // copies per thread per stage
+constexpr int kPORS = kPD + 8;                        // output staging row (bf16), padded
+constexpr float kLazyMax = 8.f;                       // log2 units the reference max may lag
+static_assert(kPIssue == 4, "two K and two V copies per thread per stage");
+static_assert(kPIssue * (kPStages - 2) <= 63, "s_waitcnt vmcnt holds 6 bits");
+static_assert(kPWaves * kPWaveRows * kPORS * 2 <= kPStages * kPStageU4 * 16, "output staging fits in the stages");
 
 typedef __bf16 pbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float pf32x16_t __attribute__((ext_vector_type(16)));
@@ -48,36 +59,107 @@ __device__ __forceinline__ int query_step(bool slot_q, int qi, const MemGeom& g)
   return slot_q ? g.S + g.W + qi * g.r : qi + 1;
 }
 
-// Key j of the block's list -> global row pointer offset: sinks and band index raw rows
-// of the prefix ([B][p_max][Hkv][D]), slots index the layer's slot rows.
+// The work-group's key list: nsink sinks (raw rows 0..), nband band rows (raw rows
+// band0..), nslot slots (slot rows 0..).
 struct PKeys {
   int nsink, band0, nband, nslot;
 };
 
-__device__ __forceinline__ const uint16_t* prefill_row(const PrefillArgs& a, const PKeys& kl, int j, int b, int kvh,
-                                                       bool v) {
-  const uint16_t* raw = static_cast<const uint16_t*>(v ? a.v : a.k);
-  const uint16_t* slot = static_cast<const uint16_t*>(v ? a.v_slot : a.k_slot);
-  if (j < kl.nsink) return raw + ((size_t(b) * a.p_max + j) * a.Hkv + kvh) * kPD;
-  j -= kl.nsink;
-  if (j < kl.nband) return raw + ((size_t(b) * a.p_max + kl.band0 + j) * a.Hkv + kvh) * kPD;
-  j -= kl.nband;
-  return slot + ((size_t(b) * a.Hkv + kvh) * a.g.max_slots + j) * kPD;
+// Element offset of key j's row: raw rows of the prefix ([B][p_max][Hkv][D], from the
+// sequence's (row 0, kvh) base) or slot rows ([B][Hkv][max_slots][D], from its base).
+__device__ __forceinline__ size_t prefill_row_off(const PKeys& kl, int j, size_t raw_stride, bool& slot) {
+  slot = j >= kl.nsink + kl.nband;
+  if (slot) return size_t(j - kl.nsink - kl.nband) * kPD;
+  return size_t(j < kl.nsink ? j : kl.band0 + (j - kl.nsink)) * raw_stride;
 }
 
-__device__ __forceinline__ void prefill_issue(u32x4_t* stage, const PrefillArgs& a, const PKeys& kl, int tile, int k0,
-                                              int k1, int b, int kvh, int lane) {
-  const int sub = lane >> 4, slot = lane & 15;
+struct PBases {
+  const uint16_t* k_raw;   // prefix rows of this (sequence, KV head)
+  const uint16_t* v_raw;
+  const uint16_t* k_slot;  // slot rows of this (sequence, KV head)
+  const uint16_t* v_slot;
+  size_t raw_stride;       // elements between consecutive positions: Hkv * D
+};
+
+// Copies keys [j0, j0 + 32) into a stage: thread t moves chunk q*256 + t of the K and of
+// the V rows, i.e. row 16 q + t/16, 16-byte slot t%16, which holds the row's chunk
+// (t%16) ^ (row%16).  Keys past the list re-read its last key (masked).  A tile inside
+// one segment takes a uniform base plus per-thread offsets; a tile across segments
+// resolves each row.
+__device__ __forceinline__ void prefill_issue(u32x4_t* stage, const PBases& pb, const PKeys& kl, int nk, int j0,
+                                              int wave, int t, const int (&off_raw)[2], const int (&off_slot)[2]) {
+  const int nraw = kl.nsink + kl.nband;
+  const int j1 = j0 + kPTile;
+  u32x4_t* dk = stage + wave * kWave;
+  u32x4_t* dv = stage + kPStageU4 / 2 + wave * kWave;
+  if (j1 <= nk && (j1 <= kl.nsink || (j0 >= kl.nsink && j1 <= nraw))) {
+    // raw rows only: sinks (raw row j) or band (raw row band0 + j - nsink)
+    const int r0 = j1 <= kl.nsink ? j0 : kl.band0 + (j0 - kl.nsink);
+    const uint16_t* kb = pb.k_raw + size_t(r0) * pb.raw_stride;
+    const uint16_t* vb = pb.v_raw + size_t(r0) * pb.raw_stride;
 #pragma unroll
-  for (int q = 0; q < kPTile / 4; ++q) {
-    const int row = 4 * q + sub;
-    const int j = tile + row < k1 ? tile + row : k0;   // rows past the range re-read a valid key (masked)
-    const int chunk = slot ^ (row & 15);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(prefill_row(a, kl, j, b, kvh, false) + chunk * 8),
-                                     (lds_ptr_t)(stage + q * kWave), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(prefill_row(a, kl, j, b, kvh, true) + chunk * 8),
-                                     (lds_ptr_t)(stage + (kPTile / 4 + q) * kWave), 16, 0, 0);
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off_raw[q]), (lds_ptr_t)(dk + q * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + off_raw[q]), (lds_ptr_t)(dv + q * 256), 16, 0, 0);
+    }
+  } else if (j1 <= nk && j0 >= nraw) {
+    const uint16_t* kb = pb.k_slot + size_t(j0 - nraw) * kPD;
+    const uint16_t* vb = pb.v_slot + size_t(j0 - nraw) * kPD;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off_slot[q]), (lds_ptr_t)(dk + q * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + off_slot[q]), (lds_ptr_t)(dv + q * 256), 16, 0, 0);
+    }
+  } else {
+    // the base is chosen as an integer (a select of the two pointers would be kept in
+    // private memory)
+    const uintptr_t kr = reinterpret_cast<uintptr_t>(pb.k_raw), ksl = reinterpret_cast<uintptr_t>(pb.k_slot);
+    const uintptr_t vr = reinterpret_cast<uintptr_t>(pb.v_raw), vsl = reinterpret_cast<uintptr_t>(pb.v_slot);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = 16 * q + (t >> 4);
+      const int chunk = (t & 15) ^ (row & 15);
+      bool slot;
+      const uintptr_t off = (prefill_row_off(kl, min(j0 + row, nk - 1), pb.raw_stride, slot) + chunk * 8) * 2;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>((slot ? ksl : kr) + off),
+                                       (lds_ptr_t)(dk + q * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>((slot ? vsl : vr) + off),
+                                       (lds_ptr_t)(dv + q * 256), 16, 0, 0);
+    }
   }
+}
+
+// Which keys of a tile [j0, j0 + 32) of the list the rows of one wave see: none, all
+// of them (every row sees every key), or some (per-element mask).
+enum TileSeen { kSeenNone = 0, kSeenAll = 1, kSeenSome = 2 };
+
+struct WaveKeys {
+  int all_sink, all_lo, all_hi, all_slot;   // seen by every row: sinks < all_sink, band raw rows
+                                            // [all_lo, all_hi), slots < all_slot
+  int any_sink, any_lo, any_hi, any_slot;   // seen by some row
+};
+
+__device__ __forceinline__ TileSeen tile_seen(const PKeys& kl, const WaveKeys& w, int nk, int j0) {
+  const int j1 = min(j0 + kPTile, nk);
+  const int nraw = kl.nsink + kl.nband;
+  // one range test per segment the tile touches; [lo, hi) clipped to each segment
+  bool any = false, all = j0 + kPTile <= nk;
+  if (j0 < kl.nsink) {
+    const int e = min(j1, kl.nsink);
+    any = any || j0 < w.any_sink;
+    all = all && e <= w.all_sink;
+  }
+  if (j1 > kl.nsink && j0 < nraw) {
+    const int s = kl.band0 + (max(j0, kl.nsink) - kl.nsink), e = kl.band0 + (min(j1, nraw) - kl.nsink);
+    any = any || (s < w.any_hi && e > w.any_lo);
+    all = all && s >= w.all_lo && e <= w.all_hi;
+  }
+  if (j1 > nraw) {
+    const int s = max(j0, nraw) - nraw, e = j1 - nraw;
+    any = any || s < w.any_slot;
+    all = all && e <= w.all_slot;
+  }
+  return !any ? kSeenNone : all ? kSeenAll : kSeenSome;
 }
 
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a) {
@@ -89,29 +171,27 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
   const int kvh = unit % a.Hkv, b = unit / a.Hkv;
   const bool slot_q = rank < a.slot_blocks;
   const int blk = slot_q ? a.slot_blocks - 1 - rank : a.raw_blocks - 1 - (rank - a.slot_blocks);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l32 = lane & 31, half = lane >> 5;
   const int G = a.Hq / a.Hkv;
   const MemGeom g = a.g;
 
-  __shared__ u32x4_t pipe[kPWaves][2][kPStageU4];           // 128 KB
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kPRows * kPRS];
-  __shared__ float sm_ml[kPWaves][kPRows][2];
+  __shared__ u32x4_t pipe[kPStages][kPStageU4];
 
   const int P = a.seq_len[b];
   if (P == 0) return;   // empty prefix: nothing to attend
   if (P < 0 || P > a.p_max) {
-    if (rank == 0 && kvh == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SEQ_RANGE);
+    if (rank == 0 && kvh == 0 && tid == 0) atomicOr(a.err, MASW_DEV_SEQ_RANGE);
     return;
   }
   const int n_all = slots_at(P, g);
   if (n_all > g.max_slots || n_all > a.ns_max) {
-    if (rank == 0 && kvh == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SLOT_CAPACITY);
+    if (rank == 0 && kvh == 0 && tid == 0) atomicOr(a.err, MASW_DEV_SLOT_CAPACITY);
     return;
   }
   if (a.n_slots[b] < n_all) {
-    if (rank == 0 && kvh == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SLOT_MISSING);
+    if (rank == 0 && kvh == 0 && tid == 0) atomicOr(a.err, MASW_DEV_SLOT_MISSING);
     return;
   }
   const int q0 = blk * a.qb;
@@ -121,49 +201,70 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
   const int R = nq * G;
   const int t_first = query_step(slot_q, q0, g), t_last = query_step(slot_q, q0 + nq - 1, g);
 
-  // Q rows into LDS (row = qi * G + gg; rows >= R are zero)
-  {
-    const uint16_t* qb = static_cast<const uint16_t*>(slot_q ? a.q_slot : a.q);
-    const int qstride = slot_q ? a.ns_max : a.p_max;
-    for (int c = threadIdx.x; c < kPRows * 16; c += kPThreads) {
-      const int row = c >> 4, ch = c & 15;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (row < R) {
-        const int qi = row / G, gg = row - (row / G) * G;
-        v = *reinterpret_cast<const u32x4_t*>(qb + ((size_t(b) * qstride + q0 + qi) * a.Hq + size_t(kvh) * G + gg) * kPD +
-                                              ch * 8);
-      }
-      *reinterpret_cast<u32x4_t*>(sQ + row * kPRS + ch * 8) = v;
-    }
-  }
-
   PKeys kl;
   kl.nsink = min(g.S, t_last);
   kl.band0 = max(g.S, t_first - g.W);
   kl.nband = max(0, t_last - kl.band0);
   kl.nslot = slots_at(t_last, g);
   const int nk = kl.nsink + kl.nband + kl.nslot;
+  const int nt = (nk + kPTile - 1) / kPTile;
 
-  // per-lane row state for each row block: step, window start, visible slots
-  int tq[kPNB], wlo[kPNB], nvis[kPNB];
+  PBases pb;
+  pb.raw_stride = size_t(a.Hkv) * kPD;
+  pb.k_raw = static_cast<const uint16_t*>(a.k) + (size_t(b) * a.p_max * a.Hkv + kvh) * kPD;
+  pb.v_raw = static_cast<const uint16_t*>(a.v) + (size_t(b) * a.p_max * a.Hkv + kvh) * kPD;
+  pb.k_slot = static_cast<const uint16_t*>(a.k_slot) + (size_t(b) * a.Hkv + kvh) * g.max_slots * kPD;
+  pb.v_slot = static_cast<const uint16_t*>(a.v_slot) + (size_t(b) * a.Hkv + kvh) * g.max_slots * kPD;
+  int off_raw[2], off_slot[2];
 #pragma unroll
-  for (int rb = 0; rb < kPNB; ++rb) {
-    const int row = rb * 32 + l32;
-    const int qi = row / G;
-    const bool ok = row < R;
-    tq[rb] = ok ? query_step(slot_q, q0 + qi, g) : 0;   // t = 0: nothing visible (padding rows)
-    wlo[rb] = max(g.S, tq[rb] - g.W);
-    nvis[rb] = ok ? slots_at(tq[rb], g) : 0;
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * q + (tid >> 4), chunk = (tid & 15) ^ (row & 15);
+    off_raw[q] = row * int(pb.raw_stride) + chunk * 8;
+    off_slot[q] = row * kPD + chunk * 8;
   }
-  // keys visible to every valid row: sinks below min(S, t_first), band rows in
-  // [max(S, t_last - W), t_first), slots below n(t_first)
-  const int all_sink = min(g.S, t_first);
-  const int all_band_lo = max(g.S, t_last - g.W), all_band_hi = t_first;
-  const int all_slot = slots_at(t_first, g);
 
-  const int sub = (nk + kPWaves * kPTile - 1) / (kPWaves * kPTile) * kPTile;
-  const int w0 = wave * sub, w1 = min(w0 + sub, nk);
-  const int nt = w0 < w1 ? (w1 - w0 + kPTile - 1) / kPTile : 0;
+  // this wave's rows [r0, r1) and the keys they see
+  const int r0 = wave * kPWaveRows;
+  const bool wave_on = r0 < R;
+  const int r1 = min(R, r0 + kPWaveRows);
+  WaveKeys wk;
+  {
+    const int tf = query_step(slot_q, q0 + r0 / G, g), tl = query_step(slot_q, q0 + (max(r1, r0 + 1) - 1) / G, g);
+    wk.all_sink = min(g.S, tf);
+    wk.all_lo = max(g.S, tl - g.W);
+    wk.all_hi = tf;
+    wk.all_slot = slots_at(tf, g);
+    wk.any_sink = min(g.S, tl);
+    wk.any_lo = max(g.S, tf - g.W);
+    wk.any_hi = tl;
+    wk.any_slot = slots_at(tl, g);
+  }
+  // per-lane row state: step, window start, visible slots (t = 0 for padding rows: no key)
+  int tq[kPNB], wlo[kPNB], nvis[kPNB];
+  u32x4_t bq[kPNB][8];   // Q^T operand: row r0 + rb*32 + l32, d = 16 ks + 8 half .. +7
+  {
+    const uint16_t* qb = static_cast<const uint16_t*>(slot_q ? a.q_slot : a.q);
+    const int qstride = slot_q ? a.ns_max : a.p_max;
+#pragma unroll
+    for (int rb = 0; rb < kPNB; ++rb) {
+      const int row = r0 + rb * 32 + l32;
+      const bool ok = row < R;
+      const int qi = row / G, gg = row - (row / G) * G;
+      tq[rb] = ok ? query_step(slot_q, q0 + qi, g) : 0;
+      wlo[rb] = max(g.S, tq[rb] - g.W);
+      nvis[rb] = ok ? slots_at(tq[rb], g) : 0;
+      const uint16_t* qrow = qb + ((size_t(b) * qstride + q0 + (ok ? qi : 0)) * a.Hq + size_t(kvh) * G + (ok ? gg : 0)) * kPD;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        bq[rb][ks] = ok ? *reinterpret_cast<const u32x4_t*>(qrow + ks * 16 + half * 8) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // the first tiles' copies (issued after the Q loads, so waiting for a tile also
+  // covers Q)
+#pragma unroll
+  for (int s = 0; s < kPStages - 1; ++s)
+    if (s < nt) prefill_issue(pipe[s], pb, kl, nk, s * kPTile, wave, tid, off_raw, off_slot);
 
   pf32x16_t o[kPNB][4];
   float m[kPNB], l[kPNB];
@@ -176,20 +277,31 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[rb][db][v] = 0.f;
   }
-  __syncthreads();   // Q staged
 
-  if (nt > 0) prefill_issue(pipe[wave][0], a, kl, w0, w0, w1, b, kvh, lane);
-  if (nt > 1) prefill_issue(pipe[wave][1], a, kl, w0 + kPTile, w0, w1, b, kvh, lane);
-  int st = 0;
   for (int i = 0; i < nt; ++i) {
-    if (i + 1 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPStageInstr));   // only tile i+1 outstanding
+    // tile i has landed (this thread's copies; the barrier covers everyone's), and every
+    // wave is done with tile i - 1, whose stage the next copies reuse
+    if (i + kPStages - 2 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPIssue * (kPStages - 2)));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    const u32x4_t* stg = pipe[wave][st];
+    __syncthreads();
+    if (i + kPStages - 1 < nt)
+      prefill_issue(pipe[(i + kPStages - 1) % kPStages], pb, kl, nk, (i + kPStages - 1) * kPTile, wave, tid, off_raw,
+                    off_slot);
+    if (!wave_on) continue;
+    const int j0 = i * kPTile;
+    const TileSeen seen = tile_seen(kl, wk, nk, j0);
+    if (seen == kSeenNone) continue;
+
+    const u32x4_t* stg = pipe[i % kPStages];
     const uint16_t* vst = reinterpret_cast<const uint16_t*>(stg + kPStageU4 / 2);
-    u32x4_t ka[8];
+    u32x4_t ka[8];   // K operand (A of S^T): key l32, d = 16 ks + 8 half .. +7
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) ka[ks] = stg[l32 * 16 + ((2 * ks + half) ^ (l32 & 15))];
-    // V^T operand via transposing reads (see verify_stream_kernel for the lane mapping)
+    // V^T operand (A of O^T): lane (l32, half) holds d = 32 db + l32 for the keys kb+0..3
+    // and kb+8..11 (kb = 16 step + 4 half), the order of the S^T registers.  Two
+    // transposing reads per operand: in each 16-lane group lane i, element e comes from
+    // source lane 4e + i/4, element i%4, so source lane j addresses key kb + (8) + j/4,
+    // columns 32 db + 16 (group%2) + 4 (j%4) .. +3 (half of one swizzled 16-byte slot).
     u32x4_t va[4][2];
     {
       const int grp = lane >> 4, j = lane & 15, hh = grp >> 1;
@@ -212,20 +324,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    const int tile = w0 + i * kPTile;
-    if (i + 2 < nt) prefill_issue(pipe[wave][st], a, kl, tile + 2 * kPTile, w0, w1, b, kvh, lane);
-    st ^= 1;
-
-    // is the whole tile visible to every valid row?
-    const int te = min(tile + kPTile, w1);
-    bool interior;
-    if (te <= kl.nsink) interior = te <= all_sink;
-    else if (tile >= kl.nsink && te <= kl.nsink + kl.nband)
-      interior = kl.band0 + (tile - kl.nsink) >= all_band_lo && kl.band0 + (te - kl.nsink) <= all_band_hi;
-    else if (tile >= kl.nsink + kl.nband) interior = te - kl.nsink - kl.nband <= all_slot;
-    else interior = false;
-    interior = interior && tile + kPTile <= w1;
 
 #pragma unroll
     for (int rb = 0; rb < kPNB; ++rb) {
@@ -233,126 +331,92 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4_t qf = *reinterpret_cast<const u32x4_t*>(sQ + (rb * 32 + l32) * kPRS + ks * 16 + half * 8);
+      for (int ks = 0; ks < 8; ++ks)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8_t, ka[ks]),
-                                                    __builtin_bit_cast(pbf16x8_t, qf), s, 0, 0, 0);
-      }
-      // S^T layout: register v holds key 8*(v/4) + 4*half + v%4 of the tile, row l32.
-      float tmax = -INFINITY;
-      if (interior) {
+                                                    __builtin_bit_cast(pbf16x8_t, bq[rb][ks]), s, 0, 0, 0);
+      // S^T layout: register v holds key j0 + 8*(v/4) + 4*half + v%4, row l32.
+      if (seen == kSeenSome) {
+        const int nraw = kl.nsink + kl.nband;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          s[v] *= a.scale_log2;
-          tmax = fmaxf(tmax, s[v]);
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = tile + 8 * (v >> 2) + 4 * half + (v & 3);
+          const int j = j0 + 8 * (v >> 2) + 4 * half + (v & 3);
           bool vis;
-          if (j >= w1) vis = false;
-          else if (j < kl.nsink) vis = j < min(g.S, tq[rb]);
-          else if (j < kl.nsink + kl.nband) {
+          if (j >= nk) vis = false;
+          else if (j < kl.nsink) vis = j < tq[rb];   // sinks: position j + 1 <= t
+          else if (j < nraw) {
             const int x = kl.band0 + j - kl.nsink;
             vis = x >= wlo[rb] && x < tq[rb];
           } else {
-            vis = j - kl.nsink - kl.nband < nvis[rb];
+            vis = j - nraw < nvis[rb];
           }
-          const float sc = vis ? s[v] * a.scale_log2 : -INFINITY;
-          s[v] = sc;
-          tmax = fmaxf(tmax, sc);
+          s[v] = vis ? s[v] : -INFINITY;
         }
       }
+      float tmax = s[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float mn = fmaxf(m[rb], tmax);
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fast_exp2(m[rb] - mref);
-      if (__any(mn != m[rb])) {
+      const float mt = tmax * a.scale_log2;   // the tile's row max, log2 units (-inf: none seen)
+      const bool grow = mt > m[rb] + kLazyMax;
+      if (__any(grow)) {
+        // 0 for a row's first keys, 1 for rows whose reference stays (also rows that have
+        // seen nothing yet: -inf - -inf would be NaN)
+        const float alpha = grow ? fast_exp2(m[rb] - mt) : 1.f;
         l[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
+        m[rb] = grow ? mt : m[rb];
       }
-      m[rb] = mn;
+      const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(s[v] - mref);
+        const float p = fast_exp2(fmaf(s[v], a.scale_log2, -mref));   // <= 2^8
         s[v] = p;
         l[rb] += p;
       }
 #pragma unroll
       for (int step = 0; step < 2; ++step) {
         const int v0 = 8 * step;
-        const u32x4_t pb = {cvt_pk_bf16(s[v0 + 0], s[v0 + 1]), cvt_pk_bf16(s[v0 + 2], s[v0 + 3]),
-                            cvt_pk_bf16(s[v0 + 4], s[v0 + 5]), cvt_pk_bf16(s[v0 + 6], s[v0 + 7])};
+        const u32x4_t pb4 = {cvt_pk_bf16(s[v0 + 0], s[v0 + 1]), cvt_pk_bf16(s[v0 + 2], s[v0 + 3]),
+                             cvt_pk_bf16(s[v0 + 4], s[v0 + 5]), cvt_pk_bf16(s[v0 + 6], s[v0 + 7])};
 #pragma unroll
         for (int db = 0; db < 4; ++db)
           o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8_t, va[db][step]),
-                                                              __builtin_bit_cast(pbf16x8_t, pb), o[rb][db], 0, 0, 0);
+                                                              __builtin_bit_cast(pbf16x8_t, pb4), o[rb][db], 0, 0, 0);
       }
     }
   }
 
+  // Normalize and write: each wave stages its rows as bf16 in LDS (the stages are free
+  // once every wave is past the loop), then stores whole 16-byte pieces of rows.
+  __syncthreads();
+  if (!wave_on) return;
+  uint16_t* so = reinterpret_cast<uint16_t*>(&pipe[0][0]) + wave * kPWaveRows * kPORS;
 #pragma unroll
-  for (int rb = 0; rb < kPNB; ++rb) l[rb] += __shfl_xor(l[rb], 32, kWave);
-  if (half == 0) {
+  for (int rb = 0; rb < kPNB; ++rb) {
+    const float lt = l[rb] + __shfl_xor(l[rb], 32, kWave);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* dst = so + (rb * 32 + l32) * kPORS + 4 * half;
 #pragma unroll
-    for (int rb = 0; rb < kPNB; ++rb) {
-      sm_ml[wave][rb * 32 + l32][0] = m[rb];
-      sm_ml[wave][rb * 32 + l32][1] = l[rb];
-    }
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<u32x2_t*>(dst + db * 32 + 8 * g4) =
+            u32x2_t{cvt_pk_bf16(o[rb][db][4 * g4] * inv, o[rb][db][4 * g4 + 1] * inv),
+                    cvt_pk_bf16(o[rb][db][4 * g4 + 2] * inv, o[rb][db][4 * g4 + 3] * inv)};
   }
-  __syncthreads();   // every wave is past its loop: the stages are free
-  // Merge the waves: each adds its rescaled O^T into one padded [rows][132] fp32 buffer,
-  // in wave order (16-byte stores, rows 4 banks apart).
-  float* acc = reinterpret_cast<float*>(&pipe[0][0][0]);
-  static_assert(kPRows * kAccRow * 4 <= int(sizeof(pipe)), "merge buffer fits in the stages");
-  for (int w = 0; w < kPWaves; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int rb = 0; rb < kPNB; ++rb) {
-        const int row = rb * 32 + l32;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < kPWaves; ++ww) M = fmaxf(M, sm_ml[ww][row][0]);
-        const float wt = fast_exp2(m[rb] - (M == -INFINITY ? 0.f : M));
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            float4* dst = reinterpret_cast<float4*>(acc + row * kAccRow + db * 32 + 8 * v4 + 4 * half);
-            float4 x = make_float4(wt * o[rb][db][4 * v4], wt * o[rb][db][4 * v4 + 1], wt * o[rb][db][4 * v4 + 2],
-                                   wt * o[rb][db][4 * v4 + 3]);
-            if (w > 0) {
-              const float4 y = *dst;
-              x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
-            }
-            *dst = x;
-          }
-      }
-    }
-    __syncthreads();
-  }
-  // out[row] = acc[row] / L, 8 columns (16 bytes of bf16) per thread
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint16_t* outp = static_cast<uint16_t*>(slot_q ? a.o_slot : a.out);
   const int ostride = slot_q ? a.ns_max : a.p_max;
-  for (int c = threadIdx.x; c < R * 16; c += kPThreads) {
-    const int row = c >> 4, ch = c & 15;
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kPWaves; ++w) M = fmaxf(M, sm_ml[w][row][0]);
-    const float Mr = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kPWaves; ++w) L = fmaf(fast_exp2(sm_ml[w][row][0] - Mr), sm_ml[w][row][1], L);
-    const float inv = 1.f / L;
-    const float4 x0 = *reinterpret_cast<const float4*>(acc + row * kAccRow + ch * 8);
-    const float4 x1 = *reinterpret_cast<const float4*>(acc + row * kAccRow + ch * 8 + 4);
-    const u32x4_t y = {cvt_pk_bf16(x0.x * inv, x0.y * inv), cvt_pk_bf16(x0.z * inv, x0.w * inv),
-                       cvt_pk_bf16(x1.x * inv, x1.y * inv), cvt_pk_bf16(x1.z * inv, x1.w * inv)};
+  for (int c = lane; c < kPWaveRows * 16; c += kWave) {
+    const int row = r0 + (c >> 4), ch = c & 15;
+    if (row >= r1) break;
     const int qi = row / G, gg = row - (row / G) * G;
     *reinterpret_cast<u32x4_t*>(outp + ((size_t(b) * ostride + q0 + qi) * a.Hq + size_t(kvh) * G + gg) * kPD +
-                                ch * 8) = y;
+                                ch * 8) = *reinterpret_cast<const u32x4_t*>(so + (c >> 4) * kPORS + ch * 8);
   }
 }
 

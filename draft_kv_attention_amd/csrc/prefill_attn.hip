@@ -10,10 +10,11 @@
 // key list is sinks ++ the raw band [max(S, t_first - W), t_last) ++ slots
 // [0, n(t_last)), each row masked to its own keylist(t_q).
 //
-// The four waves own 64 rows each (Q in registers) and walk the key list together in
-// 32-key tiles.  The work-group streams the tiles through a ring of LDS stages with
+// The eight waves own 32 rows each (Q in registers; two waves per SIMD, so one wave's
+// softmax overlaps the other's matrix work) and walk the key list together in 32-key
+// tiles.  The work-group streams the tiles through a ring of LDS stages with
 // asynchronous global->LDS copies (K rows then V rows, each row's 16-byte slots
-// XOR-swizzled by the row index), one barrier per tile; each wave computes on the
+// XOR-swizzled by a function of the row), one barrier per tile; each wave computes on the
 // matrix cores
 //   S^T[key][row] = K[key][d] . Q^T[d][row]      (v_mfma_f32_32x32x16_bf16)
 //   O^T[d][row]  += V^T[d][key] . P^T[key][row]  (V^T via ds_read_b64_tr_b16)
@@ -26,10 +27,10 @@
 namespace masw {
 namespace {
 
-constexpr int kPWaves = 4;
+constexpr int kPWaves = 8;
 constexpr int kPThreads = kPWaves * kWave;
 constexpr int kPD = 128;
-constexpr int kPNB = 2;                               // row blocks of 32 per wave
+constexpr int kPNB = 1;                               // row blocks of 32 per wave
 constexpr int kPWaveRows = kPNB * 32;
 constexpr int kPRows = kPWaves * kPWaveRows;          // rows per work-group
 constexpr int kPTile = 32;                            // keys per stage
@@ -41,7 +42,8 @@ constexpr int kPStageU4 = 2 * kPTile * kPD * 2 / 16;  // 16-byte words per stage
 constexpr int kPIssue = kPStageU4 / kPThreads;        // copies per thread per stage
 constexpr int kPORS = kPD + 8;                        // output staging row (bf16), padded
 constexpr float kLazyMax = 8.f;                       // log2 units the reference max may lag
-static_assert(kPIssue == 4, "two K and two V copies per thread per stage");
+constexpr int kPCopies = kPIssue / 2;                 // K (and V) copies per thread per stage
+static_assert(kPCopies * kPThreads * 2 == kPStageU4, "the threads cover a stage");
 static_assert(kPIssue * (kPStages - 2) <= 63, "s_waitcnt vmcnt holds 6 bits");
 static_assert(kPWaves * kPWaveRows * kPORS * 2 <= kPStages * kPStageU4 * 16, "output staging fits in the stages");
 
@@ -58,6 +60,14 @@ __device__ __forceinline__ int slots_at(int t, const MemGeom& g) {
 __device__ __forceinline__ int query_step(bool slot_q, int qi, const MemGeom& g) {
   return slot_q ? g.S + g.W + qi * g.r : qi + 1;
 }
+
+// 16-byte slot swizzle of a tile row: slot = chunk ^ tile_swz(row), the row's two low
+// bits moved above its next two.  With 64 LDS banks (256-byte rows, so slot s of every
+// row is banks 4s..4s+3) both operand reads are conflict-free: the K read's 16 lanes per
+// pass take rows 0..15 at one chunk (a bijection of the row), and the transposing V read's
+// 32 lanes take 4 consecutive keys x 4 chunks of one aligned group (the keys' swizzles
+// differ in the bits above the group).
+__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 // The work-group's key list: nsink sinks (raw rows 0..), nband band rows (raw rows
 // band0..), nslot slots (slot rows 0..).
@@ -81,13 +91,13 @@ struct PBases {
   size_t raw_stride;       // elements between consecutive positions: Hkv * D
 };
 
-// Copies keys [j0, j0 + 32) into a stage: thread t moves chunk q*256 + t of the K and of
-// the V rows, i.e. row 16 q + t/16, 16-byte slot t%16, which holds the row's chunk
-// (t%16) ^ (row%16).  Keys past the list re-read its last key (masked).  A tile inside
+// Copies keys [j0, j0 + 32) into a stage: thread t moves chunk c = q * threads + t of the
+// K and of the V rows, i.e. row c/16, 16-byte slot t%16, which holds the row's chunk
+// (t%16) ^ tile_swz(row).  Keys past the list re-read its last key (masked).  A tile inside
 // one segment takes a uniform base plus per-thread offsets; a tile across segments
 // resolves each row.
 __device__ __forceinline__ void prefill_issue(u32x4_t* stage, const PBases& pb, const PKeys& kl, int nk, int j0,
-                                              int wave, int t, const int (&off_raw)[2], const int (&off_slot)[2]) {
+                                              int wave, int t, const int (&off_raw)[kPCopies], const int (&off_slot)[kPCopies]) {
   const int nraw = kl.nsink + kl.nband;
   const int j1 = j0 + kPTile;
   u32x4_t* dk = stage + wave * kWave;
@@ -98,17 +108,17 @@ __device__ __forceinline__ void prefill_issue(u32x4_t* stage, const PBases& pb, 
     const uint16_t* kb = pb.k_raw + size_t(r0) * pb.raw_stride;
     const uint16_t* vb = pb.v_raw + size_t(r0) * pb.raw_stride;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off_raw[q]), (lds_ptr_t)(dk + q * 256), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + off_raw[q]), (lds_ptr_t)(dv + q * 256), 16, 0, 0);
+    for (int q = 0; q < kPCopies; ++q) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off_raw[q]), (lds_ptr_t)(dk + q * kPThreads), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + off_raw[q]), (lds_ptr_t)(dv + q * kPThreads), 16, 0, 0);
     }
   } else if (j1 <= nk && j0 >= nraw) {
     const uint16_t* kb = pb.k_slot + size_t(j0 - nraw) * kPD;
     const uint16_t* vb = pb.v_slot + size_t(j0 - nraw) * kPD;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off_slot[q]), (lds_ptr_t)(dk + q * 256), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + off_slot[q]), (lds_ptr_t)(dv + q * 256), 16, 0, 0);
+    for (int q = 0; q < kPCopies; ++q) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off_slot[q]), (lds_ptr_t)(dk + q * kPThreads), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + off_slot[q]), (lds_ptr_t)(dv + q * kPThreads), 16, 0, 0);
     }
   } else {
     // the base is chosen as an integer (a select of the two pointers would be kept in
@@ -116,15 +126,15 @@ __device__ __forceinline__ void prefill_issue(u32x4_t* stage, const PBases& pb, 
     const uintptr_t kr = reinterpret_cast<uintptr_t>(pb.k_raw), ksl = reinterpret_cast<uintptr_t>(pb.k_slot);
     const uintptr_t vr = reinterpret_cast<uintptr_t>(pb.v_raw), vsl = reinterpret_cast<uintptr_t>(pb.v_slot);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = 16 * q + (t >> 4);
-      const int chunk = (t & 15) ^ (row & 15);
+    for (int q = 0; q < kPCopies; ++q) {
+      const int row = (q * kPThreads + t) >> 4;
+      const int chunk = (t & 15) ^ tile_swz(row);
       bool slot;
       const uintptr_t off = (prefill_row_off(kl, min(j0 + row, nk - 1), pb.raw_stride, slot) + chunk * 8) * 2;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>((slot ? ksl : kr) + off),
-                                       (lds_ptr_t)(dk + q * 256), 16, 0, 0);
+                                       (lds_ptr_t)(dk + q * kPThreads), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>((slot ? vsl : vr) + off),
-                                       (lds_ptr_t)(dv + q * 256), 16, 0, 0);
+                                       (lds_ptr_t)(dv + q * kPThreads), 16, 0, 0);
     }
   }
 }
@@ -215,10 +225,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
   pb.v_raw = static_cast<const uint16_t*>(a.v) + (size_t(b) * a.p_max * a.Hkv + kvh) * kPD;
   pb.k_slot = static_cast<const uint16_t*>(a.k_slot) + (size_t(b) * a.Hkv + kvh) * g.max_slots * kPD;
   pb.v_slot = static_cast<const uint16_t*>(a.v_slot) + (size_t(b) * a.Hkv + kvh) * g.max_slots * kPD;
-  int off_raw[2], off_slot[2];
+  int off_raw[kPCopies], off_slot[kPCopies];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = 16 * q + (tid >> 4), chunk = (tid & 15) ^ (row & 15);
+  for (int q = 0; q < kPCopies; ++q) {
+    const int row = (q * kPThreads + tid) >> 4, chunk = (tid & 15) ^ tile_swz(row);
     off_raw[q] = row * int(pb.raw_stride) + chunk * 8;
     off_slot[q] = row * kPD + chunk * 8;
   }
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
     const uint16_t* vst = reinterpret_cast<const uint16_t*>(stg + kPStageU4 / 2);
     u32x4_t ka[8];   // K operand (A of S^T): key l32, d = 16 ks + 8 half .. +7
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) ka[ks] = stg[l32 * 16 + ((2 * ks + half) ^ (l32 & 15))];
+    for (int ks = 0; ks < 8; ++ks) ka[ks] = stg[l32 * 16 + ((2 * ks + half) ^ tile_swz(l32))];
     // V^T operand (A of O^T): lane (l32, half) holds d = 32 db + l32 for the keys kb+0..3
     // and kb+8..11 (kb = 16 step + 4 half), the order of the S^T registers.  Two
     // transposing reads per operand: in each 16-lane group lane i, element e comes from
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
           for (int part = 0; part < 2; ++part) {
             const int key = 16 * step + 4 * hh + 8 * part + (j >> 2);
-            const uint16_t* src = vst + key * kPD + ((cd ^ (key & 15)) << 3) + e;
+            const uint16_t* src = vst + key * kPD + ((cd ^ tile_swz(key)) << 3) + e;
             const u32x2_t y = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src));
             w[2 * part] = y.x;
             w[2 * part + 1] = y.y;
@@ -339,16 +349,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a)
         const int nraw = kl.nsink + kl.nband;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
+          // branch-free: sinks (position j + 1 <= t), band (raw row in [wlo, t)), slots
           const int j = j0 + 8 * (v >> 2) + 4 * half + (v & 3);
-          bool vis;
-          if (j >= nk) vis = false;
-          else if (j < kl.nsink) vis = j < tq[rb];   // sinks: position j + 1 <= t
-          else if (j < nraw) {
-            const int x = kl.band0 + j - kl.nsink;
-            vis = x >= wlo[rb] && x < tq[rb];
-          } else {
-            vis = j - nraw < nvis[rb];
-          }
+          const int x = kl.band0 + j - kl.nsink;
+          const bool in_sink = j < kl.nsink, in_band = (j >= kl.nsink) & (j < nraw), in_slot = (j >= nraw) & (j < nk);
+          const bool vis = (in_sink & (j < tq[rb])) | (in_band & (x >= wlo[rb]) & (x < tq[rb])) |
+                           (in_slot & (j - nraw < nvis[rb]));
           s[v] = vis ? s[v] : -INFINITY;
         }
       }

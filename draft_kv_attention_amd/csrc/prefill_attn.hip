@@ -6,13 +6,13 @@
 // at position i has t_q = i, slot g_m's query t_q = t_m - r (§3.2 Algorithm 1 step 2).
 //
 // Work-group = one block of QB consecutive queries (raw positions, or slot indices) of
-// one (sequence, KV head): R = QB * G <= 256 rows (query-major: row = qi * G + g).  Its
+// one (sequence, KV head): R = QB * G <= 128 rows (query-major: row = qi * G + g).  Its
 // key list is sinks ++ the raw band [max(S, t_first - W), t_last) ++ slots
 // [0, n(t_last)), each row masked to its own keylist(t_q).
 //
-// The eight waves own 32 rows each (Q in registers; two waves per SIMD, so one wave's
-// softmax overlaps the other's matrix work) and walk the key list together in 32-key
-// tiles.  The work-group streams the tiles through a ring of LDS stages with
+// The four waves own 32 rows each (Q in registers) and walk the key list together in
+// 32-key tiles; two work-groups share a CU (64 KB of LDS each), so each SIMD holds two
+// independent waves and one's softmax overlaps the other's matrix work.  The work-group streams the tiles through a ring of LDS stages with
 // asynchronous global->LDS copies (K rows then V rows, each row's 16-byte slots
 // XOR-swizzled by a function of the row), one barrier per tile; each wave computes on the
 // matrix cores
@@ -27,7 +27,10 @@
 namespace masw {
 namespace {
 
-constexpr int kPWaves = 8;
+#ifndef MASW_PREFILL_WAVES
+#define MASW_PREFILL_WAVES 4
+#endif
+constexpr int kPWaves = MASW_PREFILL_WAVES;
 constexpr int kPThreads = kPWaves * kWave;
 constexpr int kPD = 128;
 constexpr int kPNB = 1;                               // row blocks of 32 per wave
@@ -35,7 +38,7 @@ constexpr int kPWaveRows = kPNB * 32;
 constexpr int kPRows = kPWaves * kPWaveRows;          // rows per work-group
 constexpr int kPTile = 32;                            // keys per stage
 #ifndef MASW_PREFILL_STAGES
-#define MASW_PREFILL_STAGES 6
+#define MASW_PREFILL_STAGES 4
 #endif
 constexpr int kPStages = MASW_PREFILL_STAGES;
 constexpr int kPStageU4 = 2 * kPTile * kPD * 2 / 16;  // 16-byte words per stage (K then V)
@@ -172,7 +175,9 @@ __device__ __forceinline__ TileSeen tile_seen(const PKeys& kl, const WaveKeys& w
   return !any ? kSeenNone : all ? kSeenAll : kSeenSome;
 }
 
-__global__ __launch_bounds__(kPThreads) void prefill_kernel(const PrefillArgs a) {
+// Two waves per SIMD: one wave's softmax overlaps another's matrix work (with four
+// waves per work-group the second wave comes from a second resident work-group).
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillArgs a) {
   // Work-group order: slot blocks, then raw blocks, each from the last (longest key
   // list) down, with the (sequence, KV head) units innermost - the longest blocks start
   // first, and with B * Hkv a multiple of 8 each unit stays on one XCD (one L2).

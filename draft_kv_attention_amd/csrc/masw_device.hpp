@@ -155,6 +155,15 @@ __device__ __forceinline__ void reset_ticket(int32_t* counter) {
   __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte slot swizzle of a 32-key K/V tile in LDS (rows of 256 bytes, as the matrix-core
+// kernels stage them): slot = chunk ^ tile_swz(row), the row's two low
+// bits moved above its next two.  With 64 LDS banks (256-byte rows, so slot s of every
+// row is banks 4s..4s+3) both operand reads are conflict-free: the K read's 16 lanes per
+// pass take rows 0..15 at one chunk (a bijection of the row), and the transposing V read's
+// 32 lanes take 4 consecutive keys x 4 chunks of one aligned group (the keys' swizzles
+// differ in the bits above the group).
+__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
 // ---------------------------------------------------------------------------
 // Memory geometry and the key resolver (Technical Review §3.1, Eq. 4)
 // ---------------------------------------------------------------------------

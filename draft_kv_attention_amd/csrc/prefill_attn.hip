@@ -64,14 +64,6 @@ __device__ __forceinline__ int query_step(bool slot_q, int qi, const MemGeom& g)
   return slot_q ? g.S + g.W + qi * g.r : qi + 1;
 }
 
-// 16-byte slot swizzle of a tile row: slot = chunk ^ tile_swz(row), the row's two low
-// bits moved above its next two.  With 64 LDS banks (256-byte rows, so slot s of every
-// row is banks 4s..4s+3) both operand reads are conflict-free: the K read's 16 lanes per
-// pass take rows 0..15 at one chunk (a bijection of the row), and the transposing V read's
-// 32 lanes take 4 consecutive keys x 4 chunks of one aligned group (the keys' swizzles
-// differ in the bits above the group).
-__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
 // The work-group's key list: nsink sinks (raw rows 0..), nband band rows (raw rows
 // band0..), nslot slots (slot rows 0..).
 struct PKeys {

@@ -351,8 +351,9 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyArgs a) {
 // flight while the matrix cores work on the current one.
 //   stage = 16 copies of 64 lanes x 16 bytes: K rows of the tile, then V rows; row
 //   `row` of the tile is 256 contiguous bytes whose 16-byte slot s holds the row's
-//   chunk s ^ (row & 15) (the swizzle is chosen through the global address each lane
-//   fetches), so the K-operand reads (32 rows, one chunk each) hit 16 distinct slots.
+//   chunk s ^ tile_swz(row) (the swizzle is chosen through the global address each lane
+//   fetches), so neither the K-operand reads nor the transposing V-operand reads meet
+//   an LDS bank conflict.
 // Each wave computes all NB row blocks for its keys; the waves then merge through LDS.
 // ---------------------------------------------------------------------------
 constexpr int kVWaveKeys = 32;                        // keys per wave tile
@@ -367,7 +368,7 @@ __device__ __forceinline__ void verify_issue(u32x4_t* stage, const uint16_t* kba
   for (int q = 0; q < kVWaveKeys / 4; ++q) {
     const int row = 4 * q + sub;
     const int key = min(tile + row, k1 - 1);   // rows past the range re-read the last key (masked)
-    const int chunk = slot ^ (row & 15);
+    const int chunk = slot ^ tile_swz(row);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + size_t(key) * kD + chunk * 8),
                                      (lds_ptr_t)(stage + q * kWave), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + size_t(key) * kD + chunk * 8),
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
     // K operand (A of S^T): key l32, d = 16 ks + 8 half .. +7
     u32x4_t ka[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) ka[ks] = stg[l32 * 16 + ((2 * ks + half) ^ (l32 & 15))];
+    for (int ks = 0; ks < 8; ++ks) ka[ks] = stg[l32 * 16 + ((2 * ks + half) ^ tile_swz(l32))];
     // V^T operand (A of O^T): lane (l32, half) holds d = 32 db + l32 for the keys
     // kb+0..3 and kb+8..11 (kb = 16 step + 4 half), the order of the S^T registers.  Two
     // transposing reads per operand: in each 16-lane group lane i, element e comes from
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
 #pragma unroll
           for (int part = 0; part < 2; ++part) {
             const int key = 16 * step + 4 * hh + 8 * part + (j >> 2);
-            const uint16_t* src = vst + key * kD + ((cd ^ (key & 15)) << 3) + e;
+            const uint16_t* src = vst + key * kD + ((cd ^ tile_swz(key)) << 3) + e;
             const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
             const u32x2_t y = __builtin_bit_cast(u32x2_t, x);
             w[2 * part] = y.x;

@@ -357,8 +357,9 @@ def prefill_flops(P, S, W, r, Hq, D, hidden=0, n_kv=0):
 def prefill_leg(dev, reps=10):
     """Draft prefill of one layer at the 3B draft shape, B = 1, a 32768-token prefix
     (479 slots): masw_prefill (slot projection, memory load, attention of every raw and
-    slot query), and the same attention kernel as a full causal prefill (every token a
-    sink).  Matrix-core roofline: algorithmic flops / time vs the dense bf16 peak."""
+    slot query); the same call without a slot chain (sinks + window only); and the same
+    attention kernel as a full causal prefill (every token a sink).  Matrix-core
+    roofline: algorithmic flops / time vs the dense bf16 peak."""
     sh, P = SI.PREFILL_3B, SI.PREFILL_LEN
     S, W, r = sh.sink, sh.window, sh.interval
     n = n_slots_at(P, S, W, r)
@@ -390,6 +391,16 @@ def prefill_leg(dev, reps=10):
     res.update(masw_ms=round(ms, 4), masw_tokens_per_s=round(P / (ms * 1e-3), 1),
                masw_tflops=round(fl / (ms * 1e-3) / 1e12, 1),
                masw_pct_bf16_peak=round(100 * fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1))
+    # without materialization: the same sinks and window, no slot chain (the comparison
+    # the pages' Table 2 draws for prefill cost)
+    d0 = M.Dims(batch=1, n_q_heads=sh.n_q_heads, n_kv_heads=sh.n_kv_heads, head_dim=sh.head_dim, sink=S,
+                window=W, interval=0, max_slots=0, dtype=sh.dtype)
+    l0 = M.alloc_layer(d0, dev, fill=None)
+    l0.n_slots.zero_()
+    ms0 = timed(lambda: M.masw_prefill(d0, l0, seq, k, v, q, out))
+    fl0 = prefill_flops(P, S, W, 0, sh.n_q_heads, sh.head_dim)
+    res.update(no_slots_ms=round(ms0, 4), no_slots_pct_bf16_peak=round(100 * fl0 / (ms0 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
+               masw_over_no_slots=round(ms / ms0, 2))
     # the same kernels as a full causal prefill: S = P, no window beyond it, no slots
     dfull = M.Dims(batch=1, n_q_heads=sh.n_q_heads, n_kv_heads=sh.n_kv_heads, head_dim=sh.head_dim, sink=P,
                    window=1, interval=0, max_slots=0, dtype=sh.dtype)
@@ -401,7 +412,7 @@ def prefill_leg(dev, reps=10):
                full_causal_pct_bf16_peak=round(100 * flf / (msf * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
                full_over_masw=round(msf / ms, 2), algorithmic_flops_masw=fl, algorithmic_flops_full=flf,
                device_err_bits=int(seq.err.item()))
-    del layer, lfull
+    del layer, lfull, l0
     torch.cuda.empty_cache()
     return res
 

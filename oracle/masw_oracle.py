@@ -32,7 +32,16 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
       holding it are never both visible.
 * R4  g_m does not attend to itself unless ``include_self`` is set.
 * R5  The slot's query vector q_g is an input (only K/V are mirrored, Algorithm 1 step 3).
-* R6  No rotary embedding on this path (all workloads draw post-positional K/V).
+* R6  Raw K/V and all queries arrive post-positional (the caller's rotary embedding is
+      already applied); every workload draws them i.i.d.
+* R11 Slot keys are rotated only when a rotary base theta is given ([TR] §3.2 Algorithm
+      1 step 6 gives g_m the position id of the raw token right after it, a duplicate id).
+      Ids are 0-based token indices, so raw position i has id i - 1 and g_m, whose block
+      ends at position S + m r, gets id S + m r.  The rotation is RoFormer's: pairs of
+      the head vector turn by pos * theta^(-2i/D), paired either as (i, i + D/2)
+      ("rotate-half", the Llama-family layout) or as (2i, 2i + 1) ("interleaved").  It
+      is applied to the fp64 projection before the cache rounds it; values are not
+      touched.
 * R7  1 <= r <= W for a memory with a slot chain.
 * R8  r = 0 means no slot chain: the memory is sinks ++ the exact W-window, the
       sink-plus-window structure [TR] §3.1's sink bullet takes from StreamingLLM; with
@@ -197,19 +206,66 @@ def to_bf16(x) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def project_slot(h: np.ndarray, w_k: np.ndarray, w_v: np.ndarray, n_kv_heads: int,
-                 head_dim: int, bf16_cache: bool) -> Tuple[np.ndarray, np.ndarray]:
+                 head_dim: int, bf16_cache: bool, rope: Optional[Tuple[float, int]] = None,
+                 pos=None) -> Tuple[np.ndarray, np.ndarray]:
     """K_g = H_g W_K,g and V_g = H_g W_V,g (row vector H, W [hidden][Hkv*D]).
 
     KV head k is the column block k*D .. k*D+D-1.  h may carry leading batch axes;
-    returns [..., Hkv, D] each, rounded to bf16 when the cache stores bf16.
+    returns [..., Hkv, D] each, rounded to bf16 when the cache stores bf16.  With
+    rope = (theta, style) (theta > 0) K_g is rotated to position id pos (reading R11;
+    pos broadcasts against h's leading axes) before the rounding.
     """
     h = np.asarray(h, np.float64)
     lead = h.shape[:-1]
     kg = (h @ np.asarray(w_k, np.float64)).reshape(lead + (n_kv_heads, head_dim))
     vg = (h @ np.asarray(w_v, np.float64)).reshape(lead + (n_kv_heads, head_dim))
+    if rope is not None and rope[0] > 0:
+        kg = rope_rotate(kg, np.asarray(pos, np.float64)[..., None], rope[0], rope[1])
     if bf16_cache:
         kg, vg = to_bf16(kg), to_bf16(vg)
     return kg, vg
+
+
+# ---------------------------------------------------------------------------
+# Rotary position of slot keys ([TR] §3.2 Algorithm 1 step 6; reading R11)
+# ---------------------------------------------------------------------------
+
+ROPE_ROTATE_HALF, ROPE_INTERLEAVED = 0, 1
+
+
+def slot_position_id(m: int, S: int, r: int) -> int:
+    """Position id of g_m: the id of the raw token right after its block B_m (a
+    duplicate id).  With 0-based ids that token, position S + m r + 1, has id S + m r."""
+    if r < 1 or m < 1:
+        raise ValueError("slots exist only with a slot chain, from m = 1")
+    return S + m * r
+
+
+def rope_pairs(D: int, style: int) -> List[Tuple[int, int, int]]:
+    """(a, b, i): the two components of a head vector rotated together, and the
+    frequency index i of their angle."""
+    half = D // 2
+    if style == ROPE_ROTATE_HALF:
+        return [(i, i + half, i) for i in range(half)]
+    if style == ROPE_INTERLEAVED:
+        return [(2 * i, 2 * i + 1, i) for i in range(half)]
+    raise ValueError("unknown rotary pairing")
+
+
+def rope_rotate(x: np.ndarray, pos, theta: float, style: int) -> np.ndarray:
+    """Rotary embedding of head vectors x [..., D] at position id pos (a scalar, or an
+    array broadcasting against x's leading axes): each pair (x_a, x_b) turns by the
+    angle pos * theta^(-2i/D), x_a' = x_a cos - x_b sin, x_b' = x_a sin + x_b cos."""
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    pos = np.asarray(pos, np.float64)
+    out = x.copy()
+    for a, b, i in rope_pairs(D, style):
+        ang = pos * float(theta) ** (-2.0 * i / D)
+        c, s = np.cos(ang), np.sin(ang)
+        out[..., a] = x[..., a] * c - x[..., b] * s
+        out[..., b] = x[..., a] * s + x[..., b] * c
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -225,10 +281,11 @@ class DraftMemory:
     """
 
     def __init__(self, S: int, W: int, r: int, n_kv_heads: int, head_dim: int,
-                 bf16_cache: bool):
+                 bf16_cache: bool, rope_theta: float = 0.0, rope_style: int = ROPE_ROTATE_HALF):
         if not (0 <= r <= W) or S < 0 or W < 1:
             raise ValueError("need S >= 0, W >= 1 and 1 <= r <= W, or r = 0 (readings R7, R8)")
         self.S, self.W, self.r = S, W, r
+        self.rope = (rope_theta, rope_style) if rope_theta > 0 else None
         self.Hkv, self.D = n_kv_heads, head_dim
         self.bf16 = bf16_cache
         self.t = 0
@@ -261,7 +318,8 @@ class DraftMemory:
         m = self.pending_boundary()
         if not m:
             return None
-        kg, vg = project_slot(h, w_k, w_v, self.Hkv, self.D, self.bf16)
+        pos = slot_position_id(m, self.S, self.r) if self.rope else None
+        kg, vg = project_slot(h, w_k, w_v, self.Hkv, self.D, self.bf16, self.rope, pos)
         self.add_slot(m, kg, vg)
         return self.slot_query(m, q_slot, scale, include_self)
 

@@ -640,3 +640,102 @@ def test_prefill_subset_rows_equal_the_full_pass():
         np.testing.assert_array_equal(part[i - 1], full[i - 1] if i in pos else 0.0)
     for m in range(1, n + 1):
         np.testing.assert_array_equal(part_s[m - 1], full_s[m - 1] if m in sl else 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Rotary position of slot keys (reading R11, [TR] §3.2 Algorithm 1 step 6)
+# ---------------------------------------------------------------------------
+
+def test_rope_hand_example():
+    """D = 4, theta = 100, id 3, both pairings, worked by hand (tests/golden)."""
+    g = json.load(open(os.path.join(GOLDEN, "rope_hand_example.json")))
+    x = np.array(g["x"])
+    np.testing.assert_allclose(O.rope_rotate(x, g["pos"], g["theta"], O.ROPE_ROTATE_HALF), g["rotate_half"],
+                               atol=g["tolerance"])
+    np.testing.assert_allclose(O.rope_rotate(x, g["pos"], g["theta"], O.ROPE_INTERLEAVED), g["interleaved"],
+                               atol=g["tolerance"])
+    for c in g["slot_ids"]:
+        assert O.slot_position_id(c["m"], c["S"], c["r"]) == c["id"]
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_rope_is_a_complex_phase(style):
+    """Written as complex numbers z = x_a + i x_b, the rotation multiplies each pair by
+    exp(i pos theta^(-2i/D)) - a formulation independent of the sin/cos lines."""
+    rng = np.random.default_rng(3 + style)
+    D, theta = 16, 500000.0
+    x = rng.normal(size=(3, D))
+    for pos in (0, 1, 7, 40000):
+        y = O.rope_rotate(x, pos, theta, style)
+        if style == O.ROPE_ROTATE_HALF:
+            a, b = np.arange(D // 2), np.arange(D // 2) + D // 2
+        else:
+            a, b = np.arange(0, D, 2), np.arange(1, D, 2)
+        z = (x[:, a] + 1j * x[:, b]) * np.exp(1j * pos * theta ** (-2.0 * np.arange(D // 2) / D))
+        np.testing.assert_allclose(y[:, a], z.real, atol=1e-12)
+        np.testing.assert_allclose(y[:, b], z.imag, atol=1e-12)
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_rope_relative_position_and_norm(style):
+    """<R(p) q, R(p') k> depends on p - p' only, rotations keep norms, id 0 is the identity."""
+    rng = np.random.default_rng(11 + style)
+    D, theta = 128, 10000.0
+    q, k = rng.normal(size=D), rng.normal(size=D)
+    for p, pp in ((5, 2), (3000, 2997), (70, 9)):
+        lhs = O.rope_rotate(q, p, theta, style) @ O.rope_rotate(k, pp, theta, style)
+        rhs = O.rope_rotate(q, p - pp, theta, style) @ k
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(rhs))
+        assert abs(np.linalg.norm(O.rope_rotate(q, p, theta, style)) - np.linalg.norm(q)) < 1e-12 * D
+    np.testing.assert_array_equal(O.rope_rotate(q, 0, theta, style), q)
+
+
+def test_rope_pairings_differ_by_a_permutation():
+    """Interleaved pairs are the rotate-half pairs after moving component i + D/2 next
+    to component i."""
+    rng = np.random.default_rng(21)
+    D = 8
+    x = rng.normal(size=D)
+    perm = np.empty(D, dtype=int)
+    perm[0::2], perm[1::2] = np.arange(D // 2), np.arange(D // 2) + D // 2   # interleaved slot -> half slot
+    y_half = O.rope_rotate(x, 9, 100.0, O.ROPE_ROTATE_HALF)
+    y_int = O.rope_rotate(x[perm], 9, 100.0, O.ROPE_INTERLEAVED)
+    np.testing.assert_allclose(y_int, y_half[perm], atol=1e-12)
+
+
+def test_slot_position_id_is_the_next_raw_tokens_id():
+    """g_m shares its id with the raw token right after its block (0-based ids: raw
+    position i has id i - 1), so it is one past every id in B_m and equals no later raw
+    token's id but that one."""
+    for S, r in ((0, 1), (4, 64), (3, 5)):
+        for m in range(1, 9):
+            blk = O.block_positions(m, S, r)
+            sid = O.slot_position_id(m, S, r)
+            assert sid == (blk[-1] + 1) - 1
+            assert all(sid > i - 1 for i in blk)
+    with pytest.raises(ValueError):
+        O.slot_position_id(1, 4, 0)
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_materialize_rotates_slot_keys_only(style):
+    """A memory with a rotary base stores R(id(g_m)) K_g and the plain V_g; theta 0 is the
+    memory without rotation."""
+    rng = np.random.default_rng(31 + style)
+    S, W, r, Hkv, G, D, hidden = 2, 6, 3, 2, 2, 8, 5
+    wk, wv = rng.normal(size=(hidden, Hkv * D)), rng.normal(size=(hidden, Hkv * D))
+    plain = O.DraftMemory(S, W, r, Hkv, D, bf16_cache=False)
+    rot = O.DraftMemory(S, W, r, Hkv, D, bf16_cache=False, rope_theta=1000.0, rope_style=style)
+    off = O.DraftMemory(S, W, r, Hkv, D, bf16_cache=False, rope_theta=0.0, rope_style=style)
+    for t in range(1, 20):
+        kv = rng.normal(size=(2, 1, Hkv, D))
+        h, qg = rng.normal(size=hidden), rng.normal(size=(Hkv * G, D))
+        for mem in (plain, rot, off):
+            mem.append(kv[0], kv[1])
+            mem.materialize(h, wk, wv, qg, 0.5)
+    assert len(rot.slots) == 3   # boundaries 11, 14, 17
+    for m, (kg, vg) in plain.slots.items():
+        np.testing.assert_array_equal(rot.slots[m][1], vg)
+        np.testing.assert_allclose(rot.slots[m][0], O.rope_rotate(kg, O.slot_position_id(m, S, r), 1000.0, style),
+                                   atol=1e-12)
+        np.testing.assert_array_equal(off.slots[m][0], kg)

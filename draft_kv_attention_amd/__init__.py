@@ -29,6 +29,7 @@ DEV_SLOT_MISSING = 8
 
 OP_DRAFT_ATTN, OP_MATERIALIZE, OP_FULLKV_DECODE, OP_FULLKV_VERIFY = 0, 1, 2, 3
 F32, BF16 = 0, 1
+ROPE_ROTATE_HALF, ROPE_INTERLEAVED = 0, 1
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 
@@ -48,7 +49,8 @@ class _Dims(ctypes.Structure):
                 ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("interval", ctypes.c_int32), ("max_slots", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("num_splits", ctypes.c_int32), ("rollback", ctypes.c_int32)]
+                ("num_splits", ctypes.c_int32), ("rollback", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rope_style", ctypes.c_int32)]
 
 
 class _Layer(ctypes.Structure):
@@ -126,11 +128,14 @@ class Dims:
     scale: float = 0.0
     num_splits: int = 0
     rollback: int = 0
+    rope_theta: float = 0.0   # > 0: slot keys rotated to their position id (include/masw.h)
+    rope_style: int = 0       # ROPE_ROTATE_HALF or ROPE_INTERLEAVED
 
     def c(self) -> _Dims:
         return _Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.sink,
                      self.window, self.interval, self.max_slots, _DTYPES[self.dtype],
-                     float(self.scale), self.num_splits, self.rollback)
+                     float(self.scale), self.num_splits, self.rollback, float(self.rope_theta),
+                     int(self.rope_style))
 
     @property
     def ring(self) -> int:

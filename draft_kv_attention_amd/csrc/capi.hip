@@ -31,6 +31,9 @@ int check_dims(const masw_dims* d, bool masw_memory) {
     if (d->sink < 0 || d->window < 1 || d->interval < 0 || d->interval > d->window || d->max_slots < 0 ||
         d->rollback < 0 || d->rollback > kMaxRollback)
       return MASW_ERR_ARG;
+    if (!(d->rope_theta >= 0.f) || std::isinf(d->rope_theta) ||
+        (d->rope_style != MASW_ROPE_ROTATE_HALF && d->rope_style != MASW_ROPE_INTERLEAVED))
+      return MASW_ERR_ARG;
   }
   return MASW_OK;
 }
@@ -322,6 +325,8 @@ MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, cons
   pa.hidden = hidden;
   pa.k_per_split = project_k_per_split(hidden);
   pa.ksplits = project_splits(hidden);
+  pa.rope_theta = d->rope_theta;
+  pa.rope_style = d->rope_style;
   pa.counters = reinterpret_cast<int32_t*>(base + p.proj_counters);
   pa.part = reinterpret_cast<float*>(base + p.proj_part);
   if ((st = launch_project(pa, d->dtype, stream))) return st;
@@ -386,6 +391,8 @@ MASW_API int masw_prefill(const masw_dims* d, const masw_layer* L, const masw_se
     pa.ksplits = 1;
     pa.k_per_split = (hidden + 127) / 128 * 128;
     pa.prefill_ns = ns_max;
+    pa.rope_theta = d->rope_theta;
+    pa.rope_style = d->rope_style;
     if ((st = launch_project(pa, d->dtype, stream))) return st;
   }
   // 2. the raw tokens the memory keeps after the prefix (sinks and the newest C)

@@ -148,6 +148,10 @@ struct ProjectArgs {
   int ksplits, k_per_split;
   float* part;
   int32_t* counters;
+  // Rotary embedding of K_g (rope_theta > 0) at id S + m*r; rope_style 0: pairs
+  // (j, j + D/2), 1: pairs (2j, 2j + 1).
+  float rope_theta;
+  int rope_style;
   // Prefill (> 0): h holds prefill_ns slot hidden states per sequence
   // ([B][prefill_ns][hidden]); rows are (sequence, slot) pairs and every slot
   // 1..n(seq_len[b]) is projected, after which n_slots[b] = n(seq_len[b]).  Needs

@@ -42,6 +42,23 @@ __device__ __forceinline__ int prefill_slot(const ProjectArgs& a, int row, bool 
   return mi < n ? mi + 1 : 0;
 }
 
+// Rotary embedding of a slot key component ([TR] §3.2 Algorithm 1 step 6): x is the
+// component, xp its pair partner, `first` whether x is the pair's first component,
+// j the pair's frequency index and id the slot's position id.  The angle is formed and
+// turned in fp64 (id * theta^(-2j/D) reaches ~1e5 radians), the product in fp32.
+__device__ __forceinline__ float rope_turn(float x, float xp, bool first, int j, int D, int id, float theta) {
+  const double ang = double(id) * pow(double(theta), -2.0 * j / D);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  const float c = float(cs), s = float(sn);
+  return first ? x * c - xp * s : xp * s + x * c;
+}
+
+// Component d of a head vector: its rotary pair partner offset (xor) and frequency index.
+__device__ __forceinline__ int rope_partner_xor(int style, int D) { return style == 0 ? D / 2 : 1; }
+__device__ __forceinline__ int rope_freq(int d, int style, int D) { return style == 0 ? d % (D / 2) : d / 2; }
+__device__ __forceinline__ bool rope_first(int d, int style, int D) { return style == 0 ? d < D / 2 : (d & 1) == 0; }
+
 constexpr int kCols = 64;          // output columns per work-group
 constexpr int kPWaves = 4;
 constexpr int kStepK = 32;         // hidden rows per MFMA step
@@ -50,6 +67,16 @@ constexpr int kTRow = kStepK + 8;  // transposed tile row (bf16), padded: 80 byt
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Global column of local column c (0..63) of column block nblk.  With rotate-half pairs
+// at D = 128 a block takes 32 columns of a head's first half and the 32 matching ones of
+// its second half, so every rotary pair lives in one work-group (lanes c and c ^ 32);
+// otherwise blocks are 64 consecutive columns (at D = 64 that already pairs c, c ^ 32).
+__device__ __forceinline__ int proj_col(int nblk, int c, int D, bool pair_halves) {
+  if (!pair_halves || D == kCols) return nblk * kCols + c;
+  const int per_head = D / kCols, head = nblk / per_head, j = nblk - head * per_head;
+  return head * D + (c < 32 ? 32 * j + c : D / 2 + 32 * j + (c - 32));
+}
 
 __device__ __forceinline__ uint32_t u16_of(const u32x4_t& v, int e) {
   const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
@@ -112,6 +139,9 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
   const int n_steps = k_wave / kStepK;
   const int brow = bg * 16 + (lane & 15);
   const int col8 = lane & 7, kq = lane >> 3;   // loader: 8 lanes per 128-byte row segment
+  const bool rope = a.rope_theta > 0.f;
+  const bool pair_halves = rope && a.rope_style == 0;   // the same column order for K and V
+  const int wcol = proj_col(nblk, col8 * 8, a.D, pair_halves);   // 8 columns never straddle 32
 
   f32x4_t acc[4];
 #pragma unroll
@@ -128,7 +158,7 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
       for (int i = 0; i < 4; ++i) {
         const int k = kk + 4 * kq + i;
         wv[p][i] = on && k < a.hidden
-                       ? *reinterpret_cast<const u32x4_t*>(Wm + size_t(k) * N + nblk * kCols + col8 * 8)
+                       ? *reinterpret_cast<const u32x4_t*>(Wm + size_t(k) * N + wcol)
                        : u32x4_t{0, 0, 0, 0};
       }
       const int ka = kk + (lane >> 4) * 8;
@@ -199,17 +229,23 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
     }
     if (tid == 0) reset_ticket(cnt);
   }
+  // thread tid holds local column tid % 64 (its lane) of rows tid / 64 + 4 j
+  const int n = proj_col(nblk, tid % kCols, a.D, pair_halves);
+  const int kvh = n / a.D, d = n - (n / a.D) * a.D;
 #pragma unroll
   for (int j = 0; j < kOut; ++j) {
     const int idx = tid + j * kPWaves * kWave;
-    const int row = idx / kCols, col = idx % kCols;
+    const int row = idx / kCols;
     const int b = sm_b[row];
     const int m = sm_m[row];
-    if (m > 0) {
-      const int n = nblk * kCols + col;
-      const int kvh = n / a.D, d = n - (n / a.D) * a.D;
-      dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = f32_to_bf16(s[j]);
+    float x = s[j];
+    if (rope && which == 0) {   // uniform: every lane takes part in the exchange
+      const float xp = __shfl_xor(x, a.rope_style == 0 ? 32 : 1, kWave);
+      if (m > 0)
+        x = rope_turn(x, xp, rope_first(d, a.rope_style, a.D), rope_freq(d, a.rope_style, a.D), a.D,
+                      a.g.S + m * a.g.r, a.rope_theta);
     }
+    if (m > 0) dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = f32_to_bf16(x);
   }
 }
 
@@ -225,13 +261,27 @@ __global__ __launch_bounds__(256) void project_valu_kernel(const ProjectArgs a) 
   }
   if (!m) return;
   const int col = blockIdx.x * blockDim.x + threadIdx.x;
-  if (col >= 2 * N) return;
+  const bool live = col < 2 * N;
   const int which = col / N, n = col - which * N;
-  const T* Wm = static_cast<const T*>(which ? a.w_v : a.w_k);
-  const T* H = static_cast<const T*>(a.h) + size_t(b) * a.hidden;
   float s = 0.f;
-  for (int k = 0; k < a.hidden; ++k) s = fmaf(Elem<T>::to_f32(H[k]), Elem<T>::to_f32(Wm[size_t(k) * N + n]), s);
+  if (live) {
+    const T* Wm = static_cast<const T*>(which ? a.w_v : a.w_k);
+    const T* H = static_cast<const T*>(a.h) + size_t(b) * a.hidden;
+    for (int k = 0; k < a.hidden; ++k) s = fmaf(Elem<T>::to_f32(H[k]), Elem<T>::to_f32(Wm[size_t(k) * N + n]), s);
+  }
   const int kvh = n / a.D, d = n - kvh * a.D;
+  if (a.rope_theta > 0.f) {
+    // a block is 256 columns starting at a multiple of 256 and D divides 256, so the
+    // partner column (d ^ D/2, or d ^ 1) is in the block
+    __shared__ float xs[256];
+    xs[threadIdx.x] = s;
+    __syncthreads();
+    const float xp = xs[threadIdx.x ^ rope_partner_xor(a.rope_style, a.D)];
+    if (live && which == 0)
+      s = rope_turn(s, xp, rope_first(d, a.rope_style, a.D), rope_freq(d, a.rope_style, a.D), a.D, a.g.S + m * a.g.r,
+                    a.rope_theta);
+  }
+  if (!live) return;
   T* dst = static_cast<T*>(which ? a.v_slot : a.k_slot);
   dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = Elem<T>::from_f32(s);
 }

@@ -50,7 +50,7 @@ extern "C" {
 #endif
 
 #define MASW_API __attribute__((visibility("default")))
-#define MASW_ABI_VERSION 4
+#define MASW_ABI_VERSION 5
 
 /* ---- host status codes ------------------------------------------------------- */
 enum {
@@ -78,6 +78,12 @@ enum {
 
 typedef enum { MASW_F32 = 0, MASW_BF16 = 1 } masw_dtype;
 
+/* Pairing of a head vector's components in the rotary embedding of slot keys. */
+typedef enum {
+  MASW_ROPE_ROTATE_HALF = 0,  /* components i and i + D/2 turn together (Llama layout) */
+  MASW_ROPE_INTERLEAVED = 1   /* components 2i and 2i + 1 turn together               */
+} masw_rope_style;
+
 /* Geometry and memory parameters.  S, W, r and max_slots are ignored by the
  * full-KV entry points. */
 typedef struct {
@@ -102,6 +108,15 @@ typedef struct {
   int32_t rollback;    /* R >= 0 extra ring rows that keep speculative appends
                           undoable (masw_rollback): the ring holds C = W + r + R
                           rows.  0: no rollback.                                   */
+  float rope_theta;    /* rotary base for slot keys ([TR] §3.2 Algorithm 1 step 6):
+                          > 0: every projected K_g is rotated, before it is rounded
+                          into the cache, to the position id of the raw token right
+                          after its block, S + m*r (0-based ids: raw position i has
+                          id i - 1); pair (a, b) of a head vector turns by
+                          id * rope_theta^(-2j/D) for its frequency index j.
+                          0: no rotation (raw K/V and queries are always the
+                          caller's, already rotated).  V_g is never rotated.       */
+  int32_t rope_style;  /* masw_rope_style of that rotation                          */
 } masw_dims;
 
 /* One layer's compact draft memory ([TR] §3.1 Eq. 4).  Layouts (C = W + r + rollback):

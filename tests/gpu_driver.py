@@ -26,14 +26,14 @@ class LayerDriver:
 
     def __init__(self, shape: SI.DraftShape, max_slots: int, seed: int = 0, device="cuda",
                  num_splits: int = 0, oracle: bool = True, fill: float = float("nan"),
-                 copy_init_perturb=None):
+                 copy_init_perturb=None, rope_theta: float = 0.0, rope_style: int = 0):
         self.shape = shape
         self.seed = seed
         self.dev = torch.device(device)
         self.d = M.Dims(batch=shape.batch, n_q_heads=shape.n_q_heads, n_kv_heads=shape.n_kv_heads,
                         head_dim=shape.head_dim, sink=shape.sink, window=shape.window,
                         interval=shape.interval, max_slots=max_slots, dtype=shape.dtype,
-                        num_splits=num_splits)
+                        num_splits=num_splits, rope_theta=rope_theta, rope_style=rope_style)
         # unused cells start as NaN: reading a dead cell would poison the output
         self.layer = M.alloc_layer(self.d, self.dev, fill=fill)
         self.layer.n_slots.zero_()
@@ -44,7 +44,8 @@ class LayerDriver:
         self.wk_np, self.wv_np = np_in(wk).astype(np.float64), np_in(wv).astype(np.float64)
         self.bf16 = shape.dtype == torch.bfloat16
         self.mems = ([O.DraftMemory(shape.sink, shape.window, shape.interval, shape.n_kv_heads,
-                                    shape.head_dim, self.bf16) for _ in range(shape.batch)]
+                                    shape.head_dim, self.bf16, rope_theta, rope_style)
+                      for _ in range(shape.batch)]
                      if oracle else None)
         self.t = 0
         self.tokens_k = {}   # position -> [B][Hkv][D] stored values (for buffer checks)

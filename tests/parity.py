@@ -65,3 +65,19 @@ def slot_bound(h, w, n_kv_heads, head_dim):
 def bf16_ulp(x):
     """Spacing of bf16 values at |x| (8 significant bits)."""
     return np.ldexp(1.0, np.frexp(np.abs(np.asarray(x, np.float64)))[1] - 8)
+
+
+def rope_partner(D, style):
+    """Index of each head-vector component's rotary pair partner (rotate-half: d ^ D/2,
+    interleaved: d ^ 1)."""
+    return np.arange(D) ^ (D // 2 if style == 0 else 1)
+
+
+def rotated_slot_bound(h, w, n_kv_heads, head_dim, style, ref):
+    """Allowance for a rotated slot key: the fp32 dot-product bound of both components
+    of its pair (each enters with a weight |cos|, |sin| <= 1) plus the fp32 rounding of
+    the turn itself (a few 2^-24 of |x_a| + |x_b|, taken from the reference)."""
+    b = slot_bound(h, w, n_kv_heads, head_dim)
+    p = rope_partner(head_dim, style)
+    r = np.abs(np.asarray(ref, np.float64))
+    return b + b[..., p] + 2.0 ** -21 * (r + r[..., p])

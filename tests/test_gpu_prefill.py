@@ -25,7 +25,7 @@ import draft_kv_attention_amd as M
 import seeded_inputs as SI
 from oracle import masw_oracle as O
 from tests.gpu_driver import np_in
-from tests.parity import assert_close, bf16_ulp, slot_bound
+from tests.parity import assert_close, bf16_ulp, rotated_slot_bound, slot_bound
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -48,12 +48,14 @@ def _shape(Hq, Hkv, S, W, r, B, hidden=256):
 class Prefill:
     """One masw_prefill call on fresh memory, with the inputs kept for the oracle."""
 
-    def __init__(self, sh, P_list, p_max, ns_max, max_slots, seed, rollback=0, with_slots=True):
+    def __init__(self, sh, P_list, p_max, ns_max, max_slots, seed, rollback=0, with_slots=True, rope_theta=0.0,
+                 rope_style=0):
         self.sh, self.P, self.p_max, self.ns_max = sh, list(P_list), p_max, ns_max
         B = sh.batch
         self.d = M.Dims(batch=B, n_q_heads=sh.n_q_heads, n_kv_heads=sh.n_kv_heads, head_dim=sh.head_dim,
                         sink=sh.sink, window=sh.window, interval=sh.interval, max_slots=max_slots,
-                        dtype=sh.dtype, rollback=rollback)
+                        dtype=sh.dtype, rollback=rollback, rope_theta=rope_theta, rope_style=rope_style)
+        self.rope = (rope_theta, rope_style) if rope_theta > 0 else None
         self.layer = M.alloc_layer(self.d, DEV, fill=NAN)
         self.layer.n_slots.zero_()
         self.seq = M.alloc_seq(B, DEV)
@@ -81,7 +83,8 @@ class Prefill:
     def oracle_slots(self, b):
         sh = self.sh
         n = self.n(b)
-        return O.project_slot(self.hn[b, :n], self.wkn, self.wvn, sh.n_kv_heads, sh.head_dim, True)
+        ids = [O.slot_position_id(m, sh.sink, sh.interval) for m in range(1, n + 1)] if self.rope else None
+        return O.project_slot(self.hn[b, :n], self.wkn, self.wvn, sh.n_kv_heads, sh.head_dim, True, self.rope, ids)
 
     def check(self, b, positions=None, slots=None):
         sh = self.sh
@@ -103,6 +106,8 @@ class Prefill:
             # stored slot K/V: [Hkv][max_slots][D] -> [n][Hkv][D]
             for name, ref_kv, w in (("k_slot", sk, self.wkn), ("v_slot", sv, self.wvn)):
                 bound = slot_bound(self.hn[b, :n], w, sh.n_kv_heads, sh.head_dim)
+                if self.rope and name == "k_slot":
+                    bound = rotated_slot_bound(self.hn[b, :n], w, sh.n_kv_heads, sh.head_dim, self.rope[1], ref_kv)
                 got_kv = getattr(self.layer, name)[b, :, :n].float().cpu().numpy().transpose(1, 0, 2)
                 assert (np.abs(got_kv - ref_kv) <= bf16_ulp(ref_kv) + bound).all(), name
 
@@ -144,7 +149,8 @@ class Prefill:
         assert int(self.seq.err.item()) == 0
         refs = []
         for b in range(d.batch):
-            mem = O.DraftMemory(sh.sink, sh.window, sh.interval, sh.n_kv_heads, sh.head_dim, True)
+            mem = O.DraftMemory(sh.sink, sh.window, sh.interval, sh.n_kv_heads, sh.head_dim, True,
+                                *(self.rope if self.rope else ()))
             mem.append(self.kn[b, :P], self.vn[b, :P])
             if self.slots:
                 sk, sv = self.oracle_slots(b)
@@ -224,3 +230,16 @@ def test_prefill_3b_32k_sampled():
     slots = sorted({1, 2, n // 2, n - 1, n} | set(int(x) for x in rng.integers(1, n + 1, 6)))
     pf.check(0, positions=positions, slots=slots)
     pf.check_memory(0)
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_prefill_with_rotated_slot_keys(style):
+    """Slot keys rotated to their position ids (reading R11) in the prefill's projection."""
+    sh = _shape(8, 2, S=4, W=64, r=8, B=2)
+    pf = Prefill(sh, [450, 450], p_max=450, ns_max=60, max_slots=60, seed=12 + style, rope_theta=10000.0,
+                 rope_style=style)
+    assert int(pf.seq.err.item()) == 0
+    for b in range(2):
+        pf.check(b)
+        pf.check_memory(b)
+    pf.decode_next(seed=13)

@@ -512,13 +512,15 @@ def verify_leg(dev, prefix=32768, n_q=6, batch=4):
     return out
 
 
-def materialize_leg(stack, t_boundary, replays=5):
+def materialize_leg(stack, t_boundary, replays=5, dims=None):
     """One slot boundary across the 28 layers (projection + structured-mask slot query).
 
     Each replay first resets every layer's n_slots to m-1 (so the boundary is pending
     again); a graph holding only those resets is timed separately and subtracted.
+    `dims` overrides the stack's (e.g. to rotate the slot keys).
     """
     L = stack.L
+    d = dims if dims is not None else stack.d
     stack.set_position(t_boundary)
     m = (t_boundary - stack.S - stack.W) // stack.r
 
@@ -529,7 +531,7 @@ def materialize_leg(stack, t_boundary, replays=5):
     def boundary():
         resets()
         for i in range(L):
-            M.masw_materialize_slot(stack.d, stack.layers[i], stack.seq, stack.h[i], stack.wk[i], stack.wv[i],
+            M.masw_materialize_slot(d, stack.layers[i], stack.seq, stack.h[i], stack.wk[i], stack.wv[i],
                                     stack.qg[i], stack.og[i], stack.ws)
 
     times = {}
@@ -696,6 +698,9 @@ def main():
     print(f"[bench] roofline {roof}", file=sys.stderr, flush=True)
     err_bits = int(stack.seq.err.item()) | int(stack.err_full.item())
     mat = materialize_leg(stack, 2052 + 480 * 64)
+    mat_rope = materialize_leg(stack, 2052 + 480 * 64,
+                               dims=dataclasses.replace(stack.d, rope_theta=500000.0, rope_style=M.ROPE_ROTATE_HALF))
+    mat["rope_us_per_layer"] = mat_rope["us_per_layer"]
     print(f"[bench] materialization {mat}", file=sys.stderr, flush=True)
     del stack
     torch.cuda.empty_cache()

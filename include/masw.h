@@ -168,7 +168,8 @@ MASW_API int masw_evict_append(const masw_dims* dims, const masw_layer* layer,
  * m > max_slots: MASW_DEV_SLOT_CAPACITY).  For an acting sequence:
  *   1. mirrored projection (Algorithm 1 step 3): K_g = H W_K,g, V_g = H W_V,g with
  *      h [B][hidden], w_k_g, w_v_g [hidden][Hkv*D] (KV head k = columns k*D..k*D+D-1),
- *      stored (rounded to the cache dtype) into slot row m-1;
+ *      K_g rotated to position id S + m*r when dims->rope_theta > 0 (Algorithm 1
+ *      step 6), stored (rounded to the cache dtype) into slot row m-1;
  *   2. the slot query (Algorithm 1 step 2, structured mask): q_slot [B][Hq][D] attends
  *      over keylist(t - r) = sinks ++ the W-window whose oldest r tokens are the block
  *      g_m compresses ++ slots 1..m-1 (plus g_m itself if include_self != 0), and the

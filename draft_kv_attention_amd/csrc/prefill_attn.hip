@@ -12,10 +12,10 @@
 //
 // The four waves own 32 rows each (Q in registers) and walk the key list together in
 // 32-key tiles; two work-groups share a CU (64 KB of LDS each), so each SIMD holds two
-// independent waves and one's softmax overlaps the other's matrix work.  The work-group streams the tiles through a ring of LDS stages with
-// asynchronous global->LDS copies (K rows then V rows, each row's 16-byte slots
-// XOR-swizzled by a function of the row), one barrier per tile; each wave computes on the
-// matrix cores
+// independent waves and one's softmax overlaps the other's matrix work.  The work-group
+// streams the tiles through a ring of LDS stages with asynchronous global->LDS copies
+// (K rows then V rows, each row's 16-byte slots XOR-swizzled by a function of the row),
+// one barrier per tile; each wave computes on the matrix cores
 //   S^T[key][row] = K[key][d] . Q^T[d][row]      (v_mfma_f32_32x32x16_bf16)
 //   O^T[d][row]  += V^T[d][key] . P^T[key][row]  (V^T via ds_read_b64_tr_b16)
 // with an online softmax whose reference max is only raised when a row's scores exceed

@@ -11,11 +11,12 @@
 // [0, n(t_last)), each row masked to its own keylist(t_q).
 //
 // The four waves own 32 rows each (Q in registers) and walk the key list together in
-// 32-key tiles; two work-groups share a CU (64 KB of LDS each), so each SIMD holds two
+// 64-key tiles; two work-groups share a CU (64 KB of LDS each), so each SIMD holds two
 // independent waves and one's softmax overlaps the other's matrix work.  The work-group
-// streams the tiles through a ring of LDS stages with asynchronous global->LDS copies
-// (K rows then V rows, each row's 16-byte slots XOR-swizzled by a function of the row),
-// one barrier per tile; each wave computes on the matrix cores
+// streams the tiles through two LDS stages with asynchronous global->LDS copies (K rows
+// then V rows, each row's 16-byte slots XOR-swizzled by a function of the row): one
+// barrier per tile, the next tile landing while this one is computed.  Each wave
+// computes, per 32-key half of the tile, on the matrix cores
 //   S^T[key][row] = K[key][d] . Q^T[d][row]      (v_mfma_f32_32x32x16_bf16)
 //   O^T[d][row]  += V^T[d][key] . P^T[key][row]  (V^T via ds_read_b64_tr_b16)
 // with an online softmax whose reference max is only raised when a row's scores exceed
@@ -36,9 +37,13 @@ constexpr int kPD = 128;
 constexpr int kPNB = 1;                               // row blocks of 32 per wave
 constexpr int kPWaveRows = kPNB * 32;
 constexpr int kPRows = kPWaves * kPWaveRows;          // rows per work-group
-constexpr int kPTile = 32;                            // keys per stage
+#ifndef MASW_PREFILL_TILE
+#define MASW_PREFILL_TILE 64
+#endif
+constexpr int kPTile = MASW_PREFILL_TILE;             // keys per stage
+constexpr int kPSub = kPTile / 32;                    // 32-key sub-tiles per stage
 #ifndef MASW_PREFILL_STAGES
-#define MASW_PREFILL_STAGES 4
+#define MASW_PREFILL_STAGES 2
 #endif
 constexpr int kPStages = MASW_PREFILL_STAGES;
 constexpr int kPStageU4 = 2 * kPTile * kPD * 2 / 16;  // 16-byte words per stage (K then V)
@@ -48,6 +53,7 @@ constexpr float kLazyMax = 8.f;                       // log2 units the referenc
 constexpr int kPCopies = kPIssue / 2;                 // K (and V) copies per thread per stage
 static_assert(kPCopies * kPThreads * 2 == kPStageU4, "the threads cover a stage");
 static_assert(kPIssue * (kPStages - 2) <= 63, "s_waitcnt vmcnt holds 6 bits");
+static_assert(kPStages >= 2, "two stages at least");
 static_assert(kPWaves * kPWaveRows * kPORS * 2 <= kPStages * kPStageU4 * 16, "output staging fits in the stages");
 
 typedef __bf16 pbf16x8_t __attribute__((ext_vector_type(8)));
@@ -301,91 +307,81 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
     const u32x4_t* stg = pipe[i % kPStages];
     const uint16_t* vst = reinterpret_cast<const uint16_t*>(stg + kPStageU4 / 2);
-    u32x4_t ka[8];   // K operand (A of S^T): key l32, d = 16 ks + 8 half .. +7
+    const int nraw = kl.nsink + kl.nband;
+    pf32x16_t s[kPSub];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) ka[ks] = stg[l32 * 16 + ((2 * ks + half) ^ tile_swz(l32))];
-    // V^T operand (A of O^T): lane (l32, half) holds d = 32 db + l32 for the keys kb+0..3
-    // and kb+8..11 (kb = 16 step + 4 half), the order of the S^T registers.  Two
-    // transposing reads per operand: in each 16-lane group lane i, element e comes from
-    // source lane 4e + i/4, element i%4, so source lane j addresses key kb + (8) + j/4,
-    // columns 32 db + 16 (group%2) + 4 (j%4) .. +3 (half of one swizzled 16-byte slot).
-    u32x4_t va[4][2];
-    {
-      const int grp = lane >> 4, j = lane & 15, hh = grp >> 1;
+    for (int h = 0; h < kPSub; ++h) {
+      u32x4_t ka[8];   // K operand (A of S^T): key 32 h + l32, d = 16 ks + 8 half .. +7
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + (grp & 1) * 16 + 4 * (j & 3);
-        const int cd = d >> 3, e = d & 7;
+      for (int ks = 0; ks < 8; ++ks) ka[ks] = stg[(32 * h + l32) * 16 + ((2 * ks + half) ^ tile_swz(l32))];
 #pragma unroll
-        for (int step = 0; step < 2; ++step) {
+      for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8_t, ka[ks]),
+                                                       __builtin_bit_cast(pbf16x8_t, bq[0][ks]), s[h], 0, 0, 0);
+    }
+    // S^T layout: register v of sub-tile h holds key j0 + 32 h + 8*(v/4) + 4*half + v%4, row l32.
+    if (seen == kSeenSome) {
+#pragma unroll
+      for (int h = 0; h < kPSub; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          // branch-free: sinks (position j + 1 <= t), band (raw row in [wlo, t)), slots
+          const int j = j0 + 32 * h + 8 * (v >> 2) + 4 * half + (v & 3);
+          const int x = kl.band0 + j - kl.nsink;
+          const bool in_sink = j < kl.nsink, in_band = (j >= kl.nsink) & (j < nraw), in_slot = (j >= nraw) & (j < nk);
+          const bool vis = (in_sink & (j < tq[0])) | (in_band & (x >= wlo[0]) & (x < tq[0])) |
+                           (in_slot & (j - nraw < nvis[0]));
+          s[h][v] = vis ? s[h][v] : -INFINITY;
+        }
+    }
+    float tmax = s[0][0];
+#pragma unroll
+    for (int h = 0; h < kPSub; ++h)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[h][v]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float mt = tmax * a.scale_log2;   // the tile's row max, log2 units (-inf: none seen)
+    const bool grow = mt > m[0] + kLazyMax;
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2(m[0] - mt) : 1.f;
+      l[0] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[0][db] *= alpha;
+      m[0] = grow ? mt : m[0];
+    }
+    const float mref = m[0] == -INFINITY ? 0.f : m[0];
+    const int grp = lane >> 4, jj = lane & 15, hh = grp >> 1;
+#pragma unroll
+    for (int h = 0; h < kPSub; ++h) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(fmaf(s[h][v], a.scale_log2, -mref));   // <= 2^8
+        s[h][v] = p;
+        l[0] += p;
+      }
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+        const int v0 = 8 * step;
+        const u32x4_t pb4 = {cvt_pk_bf16(s[h][v0 + 0], s[h][v0 + 1]), cvt_pk_bf16(s[h][v0 + 2], s[h][v0 + 3]),
+                             cvt_pk_bf16(s[h][v0 + 4], s[h][v0 + 5]), cvt_pk_bf16(s[h][v0 + 6], s[h][v0 + 7])};
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = db * 32 + (grp & 1) * 16 + 4 * (jj & 3);
+          const int cd = d >> 3, e = d & 7;
           uint32_t w[4];
 #pragma unroll
           for (int part = 0; part < 2; ++part) {
-            const int key = 16 * step + 4 * hh + 8 * part + (j >> 2);
+            const int key = 32 * h + 16 * step + 4 * hh + 8 * part + (jj >> 2);
             const uint16_t* src = vst + key * kPD + ((cd ^ tile_swz(key)) << 3) + e;
             const u32x2_t y = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src));
             w[2 * part] = y.x;
             w[2 * part + 1] = y.y;
           }
-          va[db][step] = u32x4_t{w[0], w[1], w[2], w[3]};
+          o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]}),
+                                                             __builtin_bit_cast(pbf16x8_t, pb4), o[0][db], 0, 0, 0);
         }
-      }
-    }
-
-#pragma unroll
-    for (int rb = 0; rb < kPNB; ++rb) {
-      pf32x16_t s;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8_t, ka[ks]),
-                                                    __builtin_bit_cast(pbf16x8_t, bq[rb][ks]), s, 0, 0, 0);
-      // S^T layout: register v holds key j0 + 8*(v/4) + 4*half + v%4, row l32.
-      if (seen == kSeenSome) {
-        const int nraw = kl.nsink + kl.nband;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          // branch-free: sinks (position j + 1 <= t), band (raw row in [wlo, t)), slots
-          const int j = j0 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const int x = kl.band0 + j - kl.nsink;
-          const bool in_sink = j < kl.nsink, in_band = (j >= kl.nsink) & (j < nraw), in_slot = (j >= nraw) & (j < nk);
-          const bool vis = (in_sink & (j < tq[rb])) | (in_band & (x >= wlo[rb]) & (x < tq[rb])) |
-                           (in_slot & (j - nraw < nvis[rb]));
-          s[v] = vis ? s[v] : -INFINITY;
-        }
-      }
-      float tmax = s[0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float mt = tmax * a.scale_log2;   // the tile's row max, log2 units (-inf: none seen)
-      const bool grow = mt > m[rb] + kLazyMax;
-      if (__any(grow)) {
-        // 0 for a row's first keys, 1 for rows whose reference stays (also rows that have
-        // seen nothing yet: -inf - -inf would be NaN)
-        const float alpha = grow ? fast_exp2(m[rb] - mt) : 1.f;
-        l[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
-        m[rb] = grow ? mt : m[rb];
-      }
-      const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(fmaf(s[v], a.scale_log2, -mref));   // <= 2^8
-        s[v] = p;
-        l[rb] += p;
-      }
-#pragma unroll
-      for (int step = 0; step < 2; ++step) {
-        const int v0 = 8 * step;
-        const u32x4_t pb4 = {cvt_pk_bf16(s[v0 + 0], s[v0 + 1]), cvt_pk_bf16(s[v0 + 2], s[v0 + 3]),
-                             cvt_pk_bf16(s[v0 + 4], s[v0 + 5]), cvt_pk_bf16(s[v0 + 6], s[v0 + 7])};
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8_t, va[db][step]),
-                                                              __builtin_bit_cast(pbf16x8_t, pb4), o[rb][db], 0, 0, 0);
       }
     }
   }

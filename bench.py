@@ -506,7 +506,9 @@ def verify_leg(dev, prefix=32768, n_q=6, batch=4):
         flops = 4.0 * batch * n_q * Hq * 128 * t
         out.append(dict(shape=f"{Hq}q/8kv heads, prefix {prefix}+{n_q}, batch {batch}", us_per_layer=round(us, 2),
                         gbs=round(nbytes / us / 1e3, 1), pct_peak=round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1),
-                        tflops=round(flops / us / 1e6, 1), err_bits=int(ev.item())))
+                        tflops=round(flops / us / 1e6, 1),
+                        mfma_pct_bf16_peak=round(100 * flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 1),
+                        err_bits=int(ev.item())))
         del kv, vv
         torch.cuda.empty_cache()
     return out
@@ -701,6 +703,8 @@ def main():
     mat_rope = materialize_leg(stack, 2052 + 480 * 64,
                                dims=dataclasses.replace(stack.d, rope_theta=500000.0, rope_style=M.ROPE_ROTATE_HALF))
     mat["rope_us_per_layer"] = mat_rope["us_per_layer"]
+    # trend in the number of prior slots (the slot query's key list grows by one per slot)
+    mat["us_per_layer_by_slot"] = {m: materialize_leg(stack, 2052 + m * 64)["us_per_layer"] for m in (1, 128, 256, 480)}
     print(f"[bench] materialization {mat}", file=sys.stderr, flush=True)
     del stack
     torch.cuda.empty_cache()

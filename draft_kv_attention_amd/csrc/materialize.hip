@@ -44,15 +44,19 @@ __device__ __forceinline__ int prefill_slot(const ProjectArgs& a, int row, bool 
 
 // Rotary embedding of a slot key component ([TR] §3.2 Algorithm 1 step 6): x is the
 // component, xp its pair partner, `first` whether x is the pair's first component,
-// j the pair's frequency index and id the slot's position id.  The angle is formed and
-// turned in fp64 (id * theta^(-2j/D) reaches ~1e5 radians), the product in fp32.
-__device__ __forceinline__ float rope_turn(float x, float xp, bool first, int j, int D, int id, float theta) {
-  const double ang = double(id) * pow(double(theta), -2.0 * j / D);
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  const float c = float(cs), s = float(sn);
+// inv_freq = theta^(-2j/D) of the pair and id the slot's position id.  The angle
+// (~1e5 radians at long prefixes) is formed and reduced to [-pi, pi] in fp64, then
+// turned in fp32 (the reduced angle's rounding is ~2e-7 rad).
+__device__ __forceinline__ float rope_turn(float x, float xp, bool first, double inv_freq, int id) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  const double ang = double(id) * inv_freq;
+  const float red = float(ang - kTwoPi * rint(ang * (1.0 / kTwoPi)));
+  float s, c;
+  sincosf(red, &s, &c);
   return first ? x * c - xp * s : xp * s + x * c;
 }
+
+__device__ __forceinline__ double rope_inv_freq(int j, int D, float theta) { return pow(double(theta), -2.0 * j / D); }
 
 // Component d of a head vector: its rotary pair partner offset (xor) and frequency index.
 __device__ __forceinline__ int rope_partner_xor(int style, int D) { return style == 0 ? D / 2 : 1; }
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
   const int brow = bg * 16 + (lane & 15);
   const int col8 = lane & 7, kq = lane >> 3;   // loader: 8 lanes per 128-byte row segment
   const bool rope = a.rope_theta > 0.f;
-  const bool pair_halves = rope && a.rope_style == 0;   // the same column order for K and V
+  const bool pair_halves = rope && a.rope_style == 0 && which == 0;   // K only; V keeps whole 128-byte rows
   const int wcol = proj_col(nblk, col8 * 8, a.D, pair_halves);   // 8 columns never straddle 32
 
   f32x4_t acc[4];
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
   // thread tid holds local column tid % 64 (its lane) of rows tid / 64 + 4 j
   const int n = proj_col(nblk, tid % kCols, a.D, pair_halves);
   const int kvh = n / a.D, d = n - (n / a.D) * a.D;
+  const double inv_freq = rope && which == 0 ? rope_inv_freq(rope_freq(d, a.rope_style, a.D), a.D, a.rope_theta) : 0.0;
 #pragma unroll
   for (int j = 0; j < kOut; ++j) {
     const int idx = tid + j * kPWaves * kWave;
@@ -241,9 +246,7 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
     float x = s[j];
     if (rope && which == 0) {   // uniform: every lane takes part in the exchange
       const float xp = __shfl_xor(x, a.rope_style == 0 ? 32 : 1, kWave);
-      if (m > 0)
-        x = rope_turn(x, xp, rope_first(d, a.rope_style, a.D), rope_freq(d, a.rope_style, a.D), a.D,
-                      a.g.S + m * a.g.r, a.rope_theta);
+      if (m > 0) x = rope_turn(x, xp, rope_first(d, a.rope_style, a.D), inv_freq, a.g.S + m * a.g.r);
     }
     if (m > 0) dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = f32_to_bf16(x);
   }
@@ -278,8 +281,8 @@ __global__ __launch_bounds__(256) void project_valu_kernel(const ProjectArgs a) 
     __syncthreads();
     const float xp = xs[threadIdx.x ^ rope_partner_xor(a.rope_style, a.D)];
     if (live && which == 0)
-      s = rope_turn(s, xp, rope_first(d, a.rope_style, a.D), rope_freq(d, a.rope_style, a.D), a.D, a.g.S + m * a.g.r,
-                    a.rope_theta);
+      s = rope_turn(s, xp, rope_first(d, a.rope_style, a.D), rope_inv_freq(rope_freq(d, a.rope_style, a.D), a.D, a.rope_theta),
+                    a.g.S + m * a.g.r);
   }
   if (!live) return;
   T* dst = static_cast<T*>(which ? a.v_slot : a.k_slot);

@@ -27,7 +27,7 @@
 // round trip is needed when t changes.  With a fused append the newest n_new raw
 // tokens are read straight from the caller's k_new/v_new and split 0 writes them into
 // the memory (rows no other work-group of this launch reads).
-#include "masw_internal.hpp"
+#include "decode_args.hpp"
 
 namespace masw {
 namespace {

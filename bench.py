@@ -321,7 +321,7 @@ def rollback_leg(dev, reps=4):
 
 
 def single_sequence_leg(dev, steps=64, warmup=10):
-    """BASELINE configuration 1: one sequence at prefix 8192, K,V ~ 0.5 N(0,1), the MASW
+    """The batch-1 workload: one sequence at prefix 8192, K,V ~ 0.5 N(0,1), the MASW
     memory holding the full cache's own raw rows; MASW and full-KV graph steps over the
     same 28 layers."""
     sh, t = SI.DRAFT_3B, SI.DRAFT_3B_PREFIX

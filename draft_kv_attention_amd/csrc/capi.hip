@@ -150,7 +150,7 @@ MASW_API const char* masw_status_string(int status) {
     case MASW_ERR_SHAPE: return "unsupported shape";
     case MASW_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case MASW_ERR_LAUNCH: return "kernel launch failed";
-    case MASW_ERR_UNIMPLEMENTED: return "not implemented in this build";
+    case MASW_ERR_UNIMPLEMENTED: return "not supported by this library";
     default: return "unknown status";
   }
 }

@@ -60,7 +60,7 @@ enum {
   MASW_ERR_SHAPE = -3,         /* Hq % Hkv != 0, head_dim not 64/128, group > 8 ...   */
   MASW_ERR_WORKSPACE = -4,     /* workspace missing, too small or misaligned          */
   MASW_ERR_LAUNCH = -5,        /* hipGetLastError() reported a launch failure         */
-  MASW_ERR_UNIMPLEMENTED = -6  /* a valid request this build does not support         */
+  MASW_ERR_UNIMPLEMENTED = -6  /* a valid request the library does not support        */
 };
 
 /* ---- device error bits (OR-ed into *err) -------------------------------------- */

@@ -16,7 +16,7 @@ Notation follows [TR]: S sink tokens, W local-window width, r slot interval, t t
 number of raw tokens in the cache *including* the current query token (Eq. 2 attends
 over K_{<=t}), positions are 1-based, g_m is the m-th memory slot.
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
 
 * R0  Eq. 2's sqrt(d) uses the per-head key dimension D; query head h reads KV head
       floor(h / G) with G = Hq / Hkv (grouped-query attention).

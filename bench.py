@@ -344,6 +344,32 @@ def single_sequence_leg(dev, steps=64, warmup=10):
     return out
 
 
+def mfma_reference_leg(dev, iters=20000):
+    """Matrix-core rate this device sustains (`masw_mfma_rate`: four independent
+    32x32x16 bf16 MFMA chains per wave, register operands) with one and with two waves
+    per SIMD, and the shader clock under that load (s_memtime ticks per 100 MHz
+    s_memrealtime tick): the measured reference next to the nominal 2.5 PFLOP/s."""
+    res = {}
+    for label, wgs in (("one_wave_per_simd", 256), ("two_waves_per_simd", 512)):
+        out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+        clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+        M.mfma_rate(wgs, 100, out, clocks)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.mfma_rate(wgs, iters, out, clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = clocks.cpu().tolist()
+        flops = wgs * 4 * iters * 4 * 2 * 32 * 32 * 16
+        res[label] = dict(pflops=round(flops / (ms * 1e-3) / 1e15, 3),
+                          pct_of_nominal=round(100 * flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
+                          shader_ghz=round(c[0] / (c[1] / 100e6) / 1e9, 3) if c[1] else None,
+                          cycles_per_mfma=round(c[0] / (4 * iters), 2))
+    return res
+
+
 def prefill_flops(P, S, W, r, Hq, D, hidden=0, n_kv=0):
     """Algorithmic flops of a prefill: 4 D Hq per (query, visible key) for S = QK^T and
     O = PV, over every raw query i (keylist(i)) and slot query m (keylist(t_m - r)), plus
@@ -656,7 +682,7 @@ def main():
         profile_modes(args, dev)
         return
     if args.prefill_only:
-        print(json.dumps({"prefill": prefill_leg(dev)}), flush=True)
+        print(json.dumps({"prefill": prefill_leg(dev), "mfma_reference": mfma_reference_leg(dev)}), flush=True)
         return
     t_max = T_HEAD + args.warmup + args.steps + 8
     if not args.no_sweep:
@@ -721,6 +747,8 @@ def main():
         print(f"[bench] second workload {row}", file=sys.stderr, flush=True)
     sread = stream_read_leg(dev, roof["bytes_per_launch"])
     print(f"[bench] streaming read {sread}", file=sys.stderr, flush=True)
+    mref = mfma_reference_leg(dev)
+    print(f"[bench] matrix-core reference {mref}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -741,7 +769,7 @@ def main():
         "hbm_gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(value * sh.batch, 1),
         "fullkv_at_prefix": full_head, "sweep": sweep, "eq3_fit": fits, "device_err_bits": err_bits,
-        "batch1_prefix8192": single, "second_workloads": second, "rollback": rb, "prefill": pre, "streaming_read": sread,
+        "batch1_prefix8192": single, "second_workloads": second, "rollback": rb, "prefill": pre, "streaming_read": sread, "mfma_reference": mref,
         "materialization": mat, "verifier": ver,
         "roofline": roof, "cpu_baseline": cpu,
     }

@@ -86,6 +86,7 @@ _SIGS = {
     "masw_debug_keylist": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P]),
     "masw_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_int32, _P, _P]),
     "masw_rollback": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "masw_mfma_rate": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "masw_prefill": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
                                     ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
 }
@@ -451,6 +452,16 @@ def stream_read(buf: torch.Tensor, sums: torch.Tensor, work_groups: int = 0, str
     _check(sums, "sums", (STREAM_SUMS,), torch.int32)
     _ok("masw_stream_read", lib().masw_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
                                                    work_groups, sums.data_ptr(), _stream(stream)))
+
+
+def mfma_rate(work_groups: int, iters: int, out: torch.Tensor, clocks: torch.Tensor, stream=None) -> None:
+    """Measurement helper: matrix-core rate probe (see include/masw.h).  out float32
+    [work_groups * 256], clocks int64 [2] (shader-clock and 100 MHz real-time ticks of
+    work-group 0's first wave), both on the device."""
+    _check(out, "out", (work_groups * 256,), torch.float32)
+    _check(clocks, "clocks", (2,), torch.int64)
+    _ok("masw_mfma_rate", lib().masw_mfma_rate(work_groups, iters, out.data_ptr(), clocks.data_ptr(),
+                                               _stream(stream)))
 
 
 def status_string(st: int) -> str:

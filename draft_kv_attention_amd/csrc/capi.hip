@@ -491,6 +491,11 @@ MASW_API int fullkv_verify_attn(const masw_dims* d, const void* k, const void* v
   return MASW_OK;
 }
 
+MASW_API int masw_mfma_rate(int32_t work_groups, int32_t iters, float* out, uint64_t* clocks, hipStream_t stream) {
+  if (work_groups < 1 || iters < 1 || !out || !clocks) return MASW_ERR_ARG;
+  return launch_mfma_rate(work_groups, iters, out, clocks, stream);
+}
+
 MASW_API int masw_debug_keylist(const masw_dims* d, const masw_seq* seq, int32_t back, int32_t* out,
                                 int32_t max_keys, hipStream_t stream) {
   int st = check_dims(d, true);

@@ -99,6 +99,9 @@ struct PrefillArgs {
 };
 
 int prefill_rows_per_block();
+
+// Matrix-core rate probe (measurement helper): work_groups x 256 threads.
+int launch_mfma_rate(int work_groups, int iters, float* out, uint64_t* clocks, hipStream_t s);
 int launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 // Multi-query verifier attention over a full cache on the matrix cores (bf16, D=128,

@@ -308,6 +308,18 @@ MASW_API int masw_debug_keylist(const masw_dims* dims, const masw_seq* seq, int3
 MASW_API int masw_stream_read(const void* p, size_t bytes, int32_t work_groups, uint32_t* sums,
                               hipStream_t stream);
 
+/* Measurement helper, not part of the method: work_groups work-groups of 256 threads,
+ * each wave running iters rounds of four independent v_mfma_f32_32x32x16_bf16 on
+ * register operands (2*32*32*16 FLOP each, so 4 waves x iters x 4 x 32768 FLOP per
+ * work-group).  Every thread writes one float to out [work_groups * 256] (device; all
+ * work-groups write the same values); clocks [2] (device) receives the shader-clock and
+ * the 100 MHz real-time ticks the first wave of work-group 0 spent in its loop.  Reports
+ * the matrix-core rate and shader clock this device sustains, the measured reference
+ * for the matrix-core kernels' TFLOP/s.  work_groups >= 1 and iters >= 1, else
+ * MASW_ERR_ARG. */
+MASW_API int masw_mfma_rate(int32_t work_groups, int32_t iters, float* out, uint64_t* clocks,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

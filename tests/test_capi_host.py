@@ -129,6 +129,13 @@ def test_prefill_rejects_bad_arguments_on_host(lib):
     assert call(_dims(interval=2049)) == -1
 
 
+def test_mfma_rate_rejects_bad_arguments_on_host(lib):
+    assert lib.masw_mfma_rate(0, 10, 1 << 20, 1 << 20, None) == -1
+    assert lib.masw_mfma_rate(4, 0, 1 << 20, 1 << 20, None) == -1
+    assert lib.masw_mfma_rate(4, 10, None, 1 << 20, None) == -1
+    assert lib.masw_mfma_rate(4, 10, 1 << 20, None, None) == -1
+
+
 def test_workspace_sizes(lib):
     d = _dims(batch=8)
     a = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_DRAFT_ATTN, 0, 0)

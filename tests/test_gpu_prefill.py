@@ -243,3 +243,38 @@ def test_prefill_with_rotated_slot_keys(style):
         pf.check(b)
         pf.check_memory(b)
     pf.decode_next(seed=13)
+
+
+def test_prefill_graph_replay_matches_eager():
+    """masw_prefill captured into a HIP graph: every replay (with eager work and
+    synchronizations in between) gives the eager outputs and memory bit for bit."""
+    sh = _shape(8, 2, S=4, W=64, r=8, B=2)
+    pf = Prefill(sh, [450, 380], p_max=450, ns_max=60, max_slots=60, seed=21)
+    names = ("k_ring", "v_ring", "k_slot", "v_slot", "k_sink", "v_sink")
+    eager = (pf.out.clone(), pf.o_slot.clone(), {n: getattr(pf.layer, n).clone() for n in names},
+             pf.layer.n_slots.clone())
+    args = (pf.k.to(DEV), pf.v.to(DEV), pf.q.to(DEV))
+    slot_args = (pf.h.to(DEV), pf.wk.to(DEV), pf.wv.to(DEV), pf.qs.to(DEV))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            M.masw_prefill(pf.d, pf.layer, pf.seq, *args, pf.out, *slot_args, pf.o_slot)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        # eager work between replays: clobber the outputs and the memory
+        pf.out.fill_(float("nan"))
+        pf.o_slot.fill_(float("nan"))
+        pf.layer.k_ring.fill_(0.5 * rep)
+        pf.layer.n_slots.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(pf.seq.err.item()) == 0
+        assert torch.equal(pf.out.view(torch.int16), eager[0].view(torch.int16)), rep
+        assert torch.equal(pf.o_slot.view(torch.int16), eager[1].view(torch.int16)), rep
+        assert torch.equal(pf.layer.n_slots, eager[3]), rep
+        for n in names:   # both prefixes are longer than the ring, so every cell is refilled
+            assert torch.equal(getattr(pf.layer, n).view(torch.int16), eager[2][n].view(torch.int16)), (rep, n)

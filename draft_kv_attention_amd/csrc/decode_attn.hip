@@ -166,47 +166,67 @@ __device__ void append_rows(const DecodeArgs& a, int b, int kvh, int t, int have
 
 constexpr int kMergeBatch = 8;    // split partials one thread loads at once
 
+// Two adjacent outputs (d even) in one store.
+template <typename T>
+__device__ __forceinline__ void store_out2(T* p, float v0, float v1) {
+  if constexpr (sizeof(T) == 2)
+    *reinterpret_cast<uint32_t*>(p) = uint32_t(Elem<T>::from_f32(v0)) | (uint32_t(Elem<T>::from_f32(v1)) << 16);
+  else
+    *reinterpret_cast<float2*>(p) = make_float2(v0, v1);
+}
+
 // Combine n_valid (max, sum, o) partials of the G query heads of one KV head into out.
-// No LDS and no barrier: every thread loads, for each of its (g, d) outputs, the o
-// values and the (max, sum) pairs of a batch of splits straight into registers (all
-// loads of a batch in flight together) and folds the batch in online, rescaling what it
-// has when the running max grows.  One round trip when n_valid <= kMergeBatch.
+// No LDS and no barrier: every thread takes two adjacent outputs (g, d), (g, d + 1) and
+// loads, for a batch of splits, their o pairs and (max, sum) pairs as 8-byte words
+// straight into registers (every load of the batch, for all of the thread's outputs, in
+// flight together), then folds the batch in online, rescaling what it has when the
+// running max grows.  One round trip when n_valid <= kMergeBatch.
 template <typename T, int D, int G>
 __device__ __forceinline__ void merge_partials(const float* part_o, const float* part_ml, size_t row0, int n_splits,
                                                int n_valid, T* outb) {
-  constexpr int PER = (G * D + kDecodeThreads - 1) / kDecodeThreads;   // (g, d) outputs per thread
+  constexpr int NP = G * D / 2;                                     // output pairs
+  constexpr int PER = (NP + kDecodeThreads - 1) / kDecodeThreads;   // pairs per thread
+  float M[PER], L[PER], O0[PER], O1[PER];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int idx = threadIdx.x + k * kDecodeThreads;
-    if (PER * kDecodeThreads != G * D && idx >= G * D) break;
-    const int g = idx / D, d = idx - (idx / D) * D;
-    const float* po = part_o + (row0 + g) * n_splits * D + d;
-    const float* ml = part_ml + (row0 + g) * n_splits * 2;
-    float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < n_valid; s0 += kMergeBatch) {
-      float pm[kMergeBatch], pl[kMergeBatch], v[kMergeBatch];
+  for (int k = 0; k < PER; ++k) { M[k] = -INFINITY; L[k] = 0.f; O0[k] = 0.f; O1[k] = 0.f; }
+  for (int s0 = 0; s0 < n_valid; s0 += kMergeBatch) {
+    float2 ml[PER][kMergeBatch], v[PER][kMergeBatch];
 #pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const bool ok = s0 + j < n_valid;
-        pm[j] = ok ? load_partial(&ml[2 * (s0 + j)]) : -INFINITY;
-        pl[j] = ok ? load_partial(&ml[2 * (s0 + j) + 1]) : 0.f;
-        v[j] = ok ? load_partial(&po[size_t(s0 + j) * D]) : 0.f;
-      }
-      float mb = M;
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, pm[j]);
-      const float alpha = fast_exp2(M - mb);   // 0 on the first batch (M = -inf)
-      L *= alpha;
-      O *= alpha;
-      M = mb;
+    for (int k = 0; k < PER; ++k) {
+      const int pi = threadIdx.x + k * kDecodeThreads;
+      const int g = 2 * pi / D, d = 2 * pi - g * D;
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j) {
-        const float wt = fast_exp2(pm[j] - M);   // splits past n_valid carry -inf -> 0
-        L = fmaf(wt, pl[j], L);
-        O = fmaf(wt, v[j], O);
+        const bool ok = (PER * kDecodeThreads == NP || pi < NP) && s0 + j < n_valid;
+        ml[k][j] = ok ? load_partial2(part_ml + ((row0 + g) * n_splits + s0 + j) * 2) : make_float2(-INFINITY, 0.f);
+        v[k][j] = ok ? load_partial2(part_o + ((row0 + g) * n_splits + s0 + j) * D + d) : make_float2(0.f, 0.f);
       }
     }
-    outb[g * D + d] = Elem<T>::from_f32(O / L);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      float mb = M[k];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, ml[k][j].x);
+      const float alpha = fast_exp2(M[k] - mb);   // 0 on the first batch (M = -inf)
+      L[k] *= alpha;
+      O0[k] *= alpha;
+      O1[k] *= alpha;
+      M[k] = mb;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const float wt = fast_exp2(ml[k][j].x - mb);   // splits past n_valid carry -inf -> 0
+        L[k] = fmaf(wt, ml[k][j].y, L[k]);
+        O0[k] = fmaf(wt, v[k][j].x, O0[k]);
+        O1[k] = fmaf(wt, v[k][j].y, O1[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int pi = threadIdx.x + k * kDecodeThreads;
+    if (PER * kDecodeThreads != NP && pi >= NP) break;
+    const int g = 2 * pi / D, d = 2 * pi - g * D;
+    store_out2<T>(outb + g * D + d, O0[k] / L[k], O1[k] / L[k]);
   }
 }
 
@@ -384,6 +404,40 @@ __device__ __forceinline__ void reduce_tile(const uint32_t (&fk)[U][NW], const u
   }
 }
 
+// Sum the wave's row groups (lanes equal modulo LPR) of all G * EPL accumulators as a
+// reduce-scatter: each step pairs lanes across one lane bit (5, 4, then 3 for LPR 8),
+// and one permlane swap hands the lower half of the pair value k and the upper half
+// value k + H, so each step costs one swap and one add per two values and halves what a
+// lane holds.  Afterwards the lane of row group lgrp holds values k + NF * lgrp, k < NF
+// (value g * EPL + e at x[k]).
+template <int LPR, int G, int EPL>
+__device__ __forceinline__ void groups_reduce_scatter(float (&acc)[G][EPL], int lane) {
+  constexpr int NV = G * EPL;
+  static_assert(NV % (64 / LPR) == 0, "every row group keeps the same number of values");
+#define MASW_X(k) acc[(k) / EPL][(k) % EPL]
+#pragma unroll
+  for (int k = 0; k < NV / 2; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(MASW_X(k)), __float_as_uint(MASW_X(k + NV / 2)),
+                                                    false, false);
+    MASW_X(k) = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int k = 0; k < NV / 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(MASW_X(k)), __float_as_uint(MASW_X(k + NV / 4)),
+                                                    false, false);
+    MASW_X(k) = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (LPR == 8) {
+    const bool hi = (lane & 8) != 0;
+#pragma unroll
+    for (int k = 0; k < NV / 8; ++k) {
+      const float keep = hi ? MASW_X(k + NV / 8) : MASW_X(k), send = hi ? MASW_X(k) : MASW_X(k + NV / 8);
+      MASW_X(k) = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0x128, 0xf, 0xf, false));
+    }
+  }
+#undef MASW_X
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
   constexpr int LPR = RowLayout<T>::LPR;
@@ -524,11 +578,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 
   // Row groups of a wave share the running max; sum their partial l and o.
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    l[g] = groups_sum<LPR>(l[g]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = groups_sum<LPR>(acc[g][e]);
-  }
+  for (int g = 0; g < G; ++g) l[g] = groups_sum<LPR>(l[g]);
+  groups_reduce_scatter<LPR, G, EPL>(acc, lane);
+  constexpr int NF = G * EPL / (kWave / LPR);   // accumulators a lane keeps
 
   __shared__ float sm_m[NWAVES][G], sm_l[NWAVES][G];
   __shared__ int sm_last;
@@ -536,34 +588,36 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 #pragma unroll
     for (int g = 0; g < G; ++g) { sm_m[wave][g] = m[g]; sm_l[wave][g] = l[g]; }
   }
-  if (lane < LPR) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave * WAVE_O + g * D + (e / VEC) * CH + lsub * VEC + e % VEC] = acc[g][e];
+  for (int k = 0; k < NF; ++k) {
+    const int kk = k + NF * lgrp, g = kk / EPL, e = kk % EPL;
+    sm_o[wave * WAVE_O + g * D + (e / VEC) * CH + lsub * VEC + e % VEC] = acc[k / EPL][k % EPL];
   }
   __syncthreads();
 
   T* outb = static_cast<T*>(a.out) + size_t(b) * a.qo_stride + size_t(kvh) * G * D;
   const size_t row0 = size_t(b) * a.Hq + size_t(kvh) * G;   // partial rows of this KV head
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-    const int g = idx / D, d = idx - (idx / D) * D;
+  // Each thread combines the waves for two adjacent outputs (d, d + 1).
+  for (int pi = threadIdx.x; pi < G * D / 2; pi += kDecodeThreads) {
+    const int g = 2 * pi / D, d = 2 * pi - g * D;
     float M = sm_m[0][g];
 #pragma unroll
     for (int w = 1; w < NWAVES; ++w) M = fmaxf(M, sm_m[w][g]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f, O0 = 0.f, O1 = 0.f;
 #pragma unroll
     for (int w = 0; w < NWAVES; ++w) {
       const float wt = fast_exp2(sm_m[w][g] - M);   // idle waves carry m = -inf -> 0
+      const float2 o = *reinterpret_cast<const float2*>(&sm_o[w * WAVE_O + g * D + d]);
       L = fmaf(wt, sm_l[w][g], L);
-      O = fmaf(wt, sm_o[w * WAVE_O + g * D + d], O);
+      O0 = fmaf(wt, o.x, O0);
+      O1 = fmaf(wt, o.y, O1);
     }
     if (n_valid == 1) {
-      outb[g * D + d] = Elem<T>::from_f32(O / L);
+      store_out2<T>(outb + g * D + d, O0 / L, O1 / L);
     } else {
       const size_t pr = (row0 + g) * a.n_splits + split;
-      store_partial(&a.part_o[pr * D + d], O);
-      if (d == 0) { store_partial(&a.part_ml[pr * 2], M); store_partial(&a.part_ml[pr * 2 + 1], L); }
+      store_partial2(&a.part_o[pr * D + d], O0, O1);
+      if (d == 0) store_partial2(&a.part_ml[pr * 2], M, L);
     }
   }
   if (n_valid == 1) {

@@ -131,6 +131,25 @@ __device__ __forceinline__ float load_partial(const float* p) {
 #endif
 }
 
+// Two adjacent partial values (an 8-byte aligned pair) as one 64-bit access.
+__device__ __forceinline__ void store_partial2(float* p, float v0, float v1) {
+  const uint64_t w = (uint64_t(__float_as_uint(v1)) << 32) | __float_as_uint(v0);
+#if MASW_SPLIT_MERGE == 2
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  *reinterpret_cast<uint64_t*>(p) = w;
+#endif
+}
+
+__device__ __forceinline__ float2 load_partial2(const float* p) {
+#if MASW_SPLIT_MERGE == 2
+  const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  const uint64_t w = *reinterpret_cast<const uint64_t*>(p);
+#endif
+  return make_float2(__uint_as_float(uint32_t(w)), __uint_as_float(uint32_t(w >> 32)));
+}
+
 // Called by every thread of the work-group after its partial stores; true (for the
 // whole work-group) when this is the last of n_valid arrivals.  The last arrival
 // resets the counter with reset_ticket() once it has merged.

@@ -129,10 +129,19 @@ void fill_full_memory(DecodeArgs& a, const void* k, const void* v, int32_t max_l
   a.max_len = max_len;
 }
 
+// Tensor pointers must be 16-byte aligned: the kernels move 16-byte pieces of rows.  A
+// null pointer passes (its presence is checked where it is required).
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+template <typename... P>
+bool all_aligned16(const P*... p) {
+  return (aligned16(p) && ...);
+}
+
 int check_layer(const masw_dims* d, const masw_layer* L) {
   if (!L || !L->k_ring || !L->v_ring || !L->n_slots) return MASW_ERR_ARG;
   if (d->sink > 0 && (!L->k_sink || !L->v_sink)) return MASW_ERR_ARG;
   if (d->max_slots > 0 && (!L->k_slot || !L->v_slot)) return MASW_ERR_ARG;
+  if (!all_aligned16(L->k_ring, L->v_ring, L->k_sink, L->v_sink, L->k_slot, L->v_slot)) return MASW_ERR_ARG;
   return MASW_OK;
 }
 
@@ -182,7 +191,7 @@ MASW_API int masw_evict_append(const masw_dims* d, const masw_layer* L, const ma
   if ((st = check_layer(d, L))) return st;
   if (!seq || !seq->seq_len || !seq->err || n_new < 0) return MASW_ERR_ARG;
   if (n_new == 0) return MASW_OK;
-  if (!k_new || !v_new) return MASW_ERR_ARG;
+  if (!k_new || !v_new || !all_aligned16(k_new, v_new)) return MASW_ERR_ARG;
   AppendArgs a{};
   a.k_sink = L->k_sink ? L->k_sink : L->k_ring;
   a.v_sink = L->v_sink ? L->v_sink : L->v_ring;
@@ -210,7 +219,7 @@ MASW_API int fullkv_append(const masw_dims* d, void* k, void* v, int32_t max_len
   if (st) return st;
   if (!k || !v || !seq_len || !err || max_len < 1 || n_new < 0) return MASW_ERR_ARG;
   if (n_new == 0) return MASW_OK;
-  if (!k_new || !v_new) return MASW_ERR_ARG;
+  if (!k_new || !v_new || !all_aligned16(k, v, k_new, v_new)) return MASW_ERR_ARG;
   AppendArgs a{};
   a.k_sink = k;
   a.v_sink = v;
@@ -244,6 +253,7 @@ MASW_API int masw_decode_step(const masw_dims* d, const masw_layer* L, const mas
   if ((st = check_layer(d, L))) return st;
   if (!seq || !seq->seq_len || !seq->err || !q || !out || n_new < 0) return MASW_ERR_ARG;
   if (n_new > 0 && (!k_new || !v_new)) return MASW_ERR_ARG;
+  if (!all_aligned16(q, out, k_new, v_new)) return MASW_ERR_ARG;
   const int splits = choose_splits(d, masw_max_keys(d));
   const WsPlan p = plan_workspace(d, splits, d->n_q_heads);
   if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
@@ -275,6 +285,7 @@ MASW_API int fullkv_decode_step(const masw_dims* d, void* k, void* v, int32_t ma
   if (st) return st;
   if (!k || !v || !seq_len || !err || !q || !out || max_len < 1 || n_new < 0) return MASW_ERR_ARG;
   if (n_new > 0 && (!k_new || !v_new)) return MASW_ERR_ARG;
+  if (!all_aligned16(k, v, q, out, k_new, v_new)) return MASW_ERR_ARG;
   const int splits = choose_splits(d, max_len);
   const WsPlan p = plan_workspace(d, splits, d->n_q_heads);
   if (splits > 1 && (st = check_ws(ws, ws_bytes, p.total))) return st;
@@ -300,6 +311,7 @@ MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, cons
   if ((st = check_layer(d, L))) return st;
   if (!seq || !seq->seq_len || !seq->err || !h || !w_k_g || !w_v_g || !q_slot || !o_slot || hidden < 1)
     return MASW_ERR_ARG;
+  if (!all_aligned16(h, w_k_g, w_v_g, q_slot, o_slot)) return MASW_ERR_ARG;
   if (d->interval == 0) return MASW_ERR_ARG;   // no slot chain to materialize
   if (d->dtype == MASW_BF16 && hidden % 8) return MASW_ERR_SHAPE;
   const int splits = choose_splits(d, masw_max_keys(d));
@@ -365,6 +377,8 @@ MASW_API int masw_prefill(const masw_dims* d, const masw_layer* L, const masw_se
   if (d->dtype != MASW_BF16 || d->head_dim != 128) return MASW_ERR_UNIMPLEMENTED;
   const bool slots = d->interval > 0 && ns_max > 0;
   if (slots && (!h_slot || !w_k_g || !w_v_g || !q_slot || !o_slot || hidden < 1)) return MASW_ERR_ARG;
+  if (!all_aligned16(k, v, q, out) || (slots && !all_aligned16(h_slot, w_k_g, w_v_g, q_slot, o_slot)))
+    return MASW_ERR_ARG;
   if (slots && hidden % 8) return MASW_ERR_SHAPE;
   const int G = d->n_q_heads / d->n_kv_heads;
   const int qb = prefill_rows_per_block() / G;
@@ -445,6 +459,7 @@ MASW_API int fullkv_verify_attn(const masw_dims* d, const void* k, const void* v
   int st = check_dims(d, false);
   if (st) return st;
   if (!k || !v || !seq_len || !err || !q || !out || max_len < 1 || n_q < 1 || n_q > 16) return MASW_ERR_ARG;
+  if (!all_aligned16(k, v, q, out)) return MASW_ERR_ARG;
   const int rows = d->n_q_heads / d->n_kv_heads * n_q;
   const bool mfma = d->dtype == MASW_BF16 && d->head_dim == 128 && rows <= 64;
   int splits = choose_splits(d, max_len, mfma ? verify_resident_per_cu(rows) : kDecodeResidentPerCU);

@@ -31,6 +31,11 @@
  *    cache rows or slot stay untouched).  The caller clears *err when it wants.
  *  - Layouts are row-major with the last index contiguous.  bf16 tensors hold IEEE
  *    bfloat16 bit patterns; results are rounded to nearest-even.  Accumulation is fp32.
+ *  - Alignment: every tensor pointer (K/V caches and slots, q, out, k_new, v_new,
+ *    hidden states, projection weights, slot queries and outputs) must be 16-byte
+ *    aligned, since the kernels move rows in 16-byte pieces; a misaligned one is
+ *    rejected with MASW_ERR_ARG.  int32 arrays (seq_len, n_slots, err) need only their
+ *    natural alignment.
  *  - Workspace: ops that split the key range (flash-decoding split-K) need a scratch
  *    buffer of at least masw_workspace_bytes(...) bytes, 256-byte aligned, that no other
  *    call uses concurrently.  The caller zero-fills it once after allocating it; every

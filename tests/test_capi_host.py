@@ -77,8 +77,44 @@ def test_null_arguments_rejected_on_host(lib):
     assert lib.masw_evict_append(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq),
                                  None, None, 0, None) == 0
     assert lib.fullkv_verify_attn(ctypes.byref(d), 1, 1, 10, 1, 1, 0, 1, 1, None, 0, None) == -1
+    A = 1 << 20
     assert lib.masw_materialize_slot(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq), 3071,
-                                     1, 1, 1, 1, 1, 0, 1 << 20, 1 << 30, None) == -3
+                                     A, A, A, A, A, 0, A, 1 << 30, None) == -3
+
+
+def test_misaligned_tensors_rejected_on_host(lib):
+    """Every tensor pointer must be 16-byte aligned (the kernels move 16-byte pieces of
+    rows); a pointer off by 8 or 2 bytes is rejected with MASW_ERR_ARG before anything is
+    enqueued, for each entry point that takes tensors."""
+    A = 1 << 20
+    d = _dims()
+    need = lib.masw_workspace_bytes(ctypes.byref(d), M.OP_MATERIALIZE, 0, 0)
+    seq = M._Seq(A, A)
+    good = M._Layer(A, A, A, A, A, A, A)
+    for field in ("k_sink", "v_sink", "k_ring", "v_ring", "k_slot", "v_slot"):
+        bad = M._Layer(A, A, A, A, A, A, A)
+        setattr(bad, field, A + 8)
+        assert lib.masw_draft_attn(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(seq), A, A, A, need, None) == -1, field
+        assert lib.masw_evict_append(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(seq), A, A, 1, None) == -1, field
+    lay, sq = ctypes.byref(good), ctypes.byref(seq)
+    for q, out in ((A + 8, A), (A, A + 2)):
+        assert lib.masw_draft_attn(ctypes.byref(d), lay, sq, q, out, A, need, None) == -1
+        assert lib.fullkv_decode_attn(ctypes.byref(d), A, A, 4096, A, A, q, out, A, need, None) == -1
+        assert lib.fullkv_verify_attn(ctypes.byref(d), A, A, 4096, A, A, 2, q, out, A, need, None) == -1
+    for kn, vn in ((A + 8, A), (A, A + 4)):
+        assert lib.masw_decode_step(ctypes.byref(d), lay, sq, kn, vn, 1, A, A, A, need, None) == -1
+        assert lib.masw_evict_append(ctypes.byref(d), lay, sq, kn, vn, 1, None) == -1
+        assert lib.fullkv_append(ctypes.byref(d), A, A, 4096, A, A, kn, vn, 1, None) == -1
+    assert lib.fullkv_decode_attn(ctypes.byref(d), A + 8, A, 4096, A, A, A, A, A, need, None) == -1
+    for i in range(5):   # h, w_k_g, w_v_g, q_slot, o_slot
+        ptrs = [A] * 5
+        ptrs[i] = A + 8
+        assert lib.masw_materialize_slot(ctypes.byref(d), lay, sq, 3072, *ptrs, 0, A, need, None) == -1, i
+        assert lib.masw_prefill(ctypes.byref(d), lay, sq, 100, A, A, A, A, 4, 3072, *ptrs, None) == -1, i
+    for i in range(4):   # k, v, q, out of the prefill
+        ptrs = [A] * 4
+        ptrs[i] = A + 8
+        assert lib.masw_prefill(ctypes.byref(d), lay, sq, 100, *ptrs, 4, 3072, A, A, A, A, A, None) == -1, i
 
 
 def test_stream_read_rejects_bad_sizes_on_host(lib):
@@ -95,8 +131,9 @@ def test_no_slot_chain_has_nothing_to_materialize(lib):
     assert lib.masw_workspace_bytes(ctypes.byref(d), M.OP_DRAFT_ATTN, 0, 0) > 0
     layer = M._Layer(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
     seq = M._Seq(1 << 20, 1 << 20)
+    A = 1 << 20
     assert lib.masw_materialize_slot(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq), 3072,
-                                     1, 1, 1, 1, 1, 0, 1 << 20, 1 << 30, None) == -1
+                                     A, A, A, A, A, 0, A, 1 << 30, None) == -1
 
 
 def test_rollback_rejects_bad_arguments_on_host(lib):

@@ -173,6 +173,27 @@ __device__ __forceinline__ TileSeen tile_seen(const PKeys& kl, const WaveKeys& w
   return !any ? kSeenNone : all ? kSeenAll : kSeenSome;
 }
 
+// Visible keys of one lane's row as offsets c from its first register key: sinks
+// [s_lo, s_lo + s_n), band [b_lo, b_lo + b_n), slots [l_lo, l_lo + l_n) (empty when n = 0).
+struct TileRanges {
+  int s_lo, s_n, b_lo, b_n, l_lo, l_n;
+};
+
+// Scores of keys the row does not see become -inf: one unsigned range test per segment
+// the tile touches, against the register's constant offset.
+template <bool TS, bool TB, bool TL>
+__device__ __forceinline__ void mask_tile(pf32x16_t (&s)[kPSub], const TileRanges& r) {
+#pragma unroll
+  for (int h = 0; h < kPSub; ++h)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int c = 32 * h + 8 * (v >> 2) + (v & 3);
+      const bool vis = (TS && unsigned(c - r.s_lo) < unsigned(r.s_n)) || (TB && unsigned(c - r.b_lo) < unsigned(r.b_n)) ||
+                       (TL && unsigned(c - r.l_lo) < unsigned(r.l_n));
+      s[h][v] = vis ? s[h][v] : -INFINITY;
+    }
+}
+
 // Two waves per SIMD: one wave's softmax overlaps another's matrix work (with four
 // waves per work-group the second wave comes from a second resident work-group).
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillArgs a) {
@@ -323,18 +344,25 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     }
     // S^T layout: register v of sub-tile h holds key j0 + 32 h + 8*(v/4) + 4*half + v%4, row l32.
     if (seen == kSeenSome) {
-#pragma unroll
-      for (int h = 0; h < kPSub; ++h)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          // branch-free: sinks (position j + 1 <= t), band (raw row in [wlo, t)), slots
-          const int j = j0 + 32 * h + 8 * (v >> 2) + 4 * half + (v & 3);
-          const int x = kl.band0 + j - kl.nsink;
-          const bool in_sink = j < kl.nsink, in_band = (j >= kl.nsink) & (j < nraw), in_slot = (j >= nraw) & (j < nk);
-          const bool vis = (in_sink & (j < tq[0])) | (in_band & (x >= wlo[0]) & (x < tq[0])) |
-                           (in_slot & (j - nraw < nvis[0]));
-          s[h][v] = vis ? s[h][v] : -INFINITY;
-        }
+      // The keys a row sees are up to three ranges of the list (its sinks, its window
+      // in the band, its slots); register v of sub-tile h holds key jb + c with the
+      // constant c = 32 h + 8 (v / 4) + v % 4.  Only the segments the tile touches
+      // (wave-uniform) are tested.
+      const int jb = j0 + 4 * half;
+      const int wl = max(wlo[0], kl.band0);
+      const TileRanges tr{-jb, min(kl.nsink, tq[0]),
+                          kl.nsink + (wl - kl.band0) - jb, max(0, min(tq[0], kl.band0 + kl.nband) - wl),
+                          nraw - jb, nvis[0]};
+      const int touch = (j0 < kl.nsink ? 1 : 0) | (j0 < nraw && j0 + kPTile > kl.nsink ? 2 : 0) |
+                        (j0 + kPTile > nraw ? 4 : 0);
+      switch (touch) {
+        case 1: mask_tile<true, false, false>(s, tr); break;
+        case 2: mask_tile<false, true, false>(s, tr); break;
+        case 3: mask_tile<true, true, false>(s, tr); break;
+        case 4: mask_tile<false, false, true>(s, tr); break;
+        case 6: mask_tile<false, true, true>(s, tr); break;
+        default: mask_tile<true, true, true>(s, tr); break;
+      }
     }
     float tmax = s[0][0];
 #pragma unroll

@@ -22,7 +22,8 @@
 // with an online softmax whose reference max is only raised when a row's scores exceed
 // it by more than 2^8 (the rescale of the accumulators is then rare; the result is the
 // same softmax), skipping tiles none of its rows can see and masking only tiles that
-// not all of its rows see whole.
+// not all of its rows see whole.  P is rounded to bf16 for the second product, and the
+// row sums add those same rounded weights (v_dot2_f32_bf16 against ones).
 #include "masw_internal.hpp"
 
 namespace masw {
@@ -301,11 +302,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     if (s < nt) prefill_issue(pipe[s], pb, kl, nk, s * kPTile, wave, tid, off_raw, off_slot);
 
   pf32x16_t o[kPNB][4];
-  float m[kPNB], l[kPNB];
+  float m[kPNB], l[kPNB][4];   // row sums in four independent partial sums
 #pragma unroll
   for (int rb = 0; rb < kPNB; ++rb) {
     m[rb] = -INFINITY;
-    l[rb] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) l[rb][k] = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -369,12 +371,13 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     for (int h = 0; h < kPSub; ++h)
 #pragma unroll
       for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[h][v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    tmax = max_xor32(tmax);   // the row's other 32 keys sit in lane ^ 32
     const float mt = tmax * a.scale_log2;   // the tile's row max, log2 units (-inf: none seen)
     const bool grow = mt > m[0] + kLazyMax;
     if (__any(grow)) {
       const float alpha = grow ? fast_exp2(m[0] - mt) : 1.f;
-      l[0] *= alpha;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) l[0][k] *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[0][db] *= alpha;
       m[0] = grow ? mt : m[0];
@@ -385,15 +388,23 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     for (int h = 0; h < kPSub; ++h) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(fmaf(s[h][v], a.scale_log2, -mref));   // <= 2^8
-        s[h][v] = p;
-        l[0] += p;
+        s[h][v] = fast_exp2(fmaf(s[h][v], a.scale_log2, -mref));   // <= 2^8
       }
 #pragma unroll
       for (int step = 0; step < 2; ++step) {
         const int v0 = 8 * step;
-        const u32x4_t pb4 = {cvt_pk_bf16(s[h][v0 + 0], s[h][v0 + 1]), cvt_pk_bf16(s[h][v0 + 2], s[h][v0 + 3]),
-                             cvt_pk_bf16(s[h][v0 + 4], s[h][v0 + 5]), cvt_pk_bf16(s[h][v0 + 6], s[h][v0 + 7])};
+        uint32_t pw[4];   // P^T operand: keys v0 .. v0 + 7 of this lane's row, bf16 pairs
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pw[k] = cvt_pk_bf16(s[h][v0 + 2 * k], s[h][v0 + 2 * k + 1]);
+        const u32x4_t pb4 = {pw[0], pw[1], pw[2], pw[3]};
+        // the row sum adds the same bf16 weights that multiply V, two per v_dot2 (each
+        // word is bit-cast from its own scalar: a bit cast of a vector element such as
+        // pb4.y has compiled to a cast of element 0)
+        const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          l[0][step + 2 * (k >> 1)] =
+              __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[k]), one2, l[0][step + 2 * (k >> 1)], false);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int d = db * 32 + (grp & 1) * 16 + 4 * (jj & 3);
@@ -421,7 +432,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   uint16_t* so = reinterpret_cast<uint16_t*>(&pipe[0][0]) + wave * kPWaveRows * kPORS;
 #pragma unroll
   for (int rb = 0; rb < kPNB; ++rb) {
-    const float lt = l[rb] + __shfl_xor(l[rb], 32, kWave);
+    const float lw = (l[rb][0] + l[rb][1]) + (l[rb][2] + l[rb][3]);
+    const float lt = lw + __shfl_xor(lw, 32, kWave);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     uint16_t* dst = so + (rb * 32 + l32) * kPORS + 4 * half;
 #pragma unroll

@@ -195,6 +195,29 @@ __device__ __forceinline__ void mask_tile(pf32x16_t (&s)[kPSub], const TileRange
     }
 }
 
+// Scores of a partly seen tile that the row does not see become -inf.  The keys a row
+// sees are up to three ranges of the list (its sinks, its window in the band, its
+// slots); register v of sub-tile h holds key jb + c with the constant
+// c = 32 h + 8 (v / 4) + v % 4.  Only the segments the tile touches (wave-uniform) are
+// tested.
+__device__ __forceinline__ void mask_scores(pf32x16_t (&s)[kPSub], const PKeys& kl, int j0, int half, int tq, int wlo,
+                                            int nvis) {
+  const int nraw = kl.nsink + kl.nband;
+  const int jb = j0 + 4 * half;
+  const int wl = max(wlo, kl.band0);
+  const TileRanges tr{-jb, min(kl.nsink, tq), kl.nsink + (wl - kl.band0) - jb,
+                      max(0, min(tq, kl.band0 + kl.nband) - wl), nraw - jb, nvis};
+  const int touch = (j0 < kl.nsink ? 1 : 0) | (j0 < nraw && j0 + kPTile > kl.nsink ? 2 : 0) | (j0 + kPTile > nraw ? 4 : 0);
+  switch (touch) {
+    case 1: mask_tile<true, false, false>(s, tr); break;
+    case 2: mask_tile<false, true, false>(s, tr); break;
+    case 3: mask_tile<true, true, false>(s, tr); break;
+    case 4: mask_tile<false, false, true>(s, tr); break;
+    case 6: mask_tile<false, true, true>(s, tr); break;
+    default: mask_tile<true, true, true>(s, tr); break;
+  }
+}
+
 // Two waves per SIMD: one wave's softmax overlaps another's matrix work (with four
 // waves per work-group the second wave comes from a second resident work-group).
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillArgs a) {
@@ -330,7 +353,6 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
     const u32x4_t* stg = pipe[i % kPStages];
     const uint16_t* vst = reinterpret_cast<const uint16_t*>(stg + kPStageU4 / 2);
-    const int nraw = kl.nsink + kl.nband;
     pf32x16_t s[kPSub];
 #pragma unroll
     for (int h = 0; h < kPSub; ++h) {
@@ -345,27 +367,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
                                                        __builtin_bit_cast(pbf16x8_t, bq[0][ks]), s[h], 0, 0, 0);
     }
     // S^T layout: register v of sub-tile h holds key j0 + 32 h + 8*(v/4) + 4*half + v%4, row l32.
-    if (seen == kSeenSome) {
-      // The keys a row sees are up to three ranges of the list (its sinks, its window
-      // in the band, its slots); register v of sub-tile h holds key jb + c with the
-      // constant c = 32 h + 8 (v / 4) + v % 4.  Only the segments the tile touches
-      // (wave-uniform) are tested.
-      const int jb = j0 + 4 * half;
-      const int wl = max(wlo[0], kl.band0);
-      const TileRanges tr{-jb, min(kl.nsink, tq[0]),
-                          kl.nsink + (wl - kl.band0) - jb, max(0, min(tq[0], kl.band0 + kl.nband) - wl),
-                          nraw - jb, nvis[0]};
-      const int touch = (j0 < kl.nsink ? 1 : 0) | (j0 < nraw && j0 + kPTile > kl.nsink ? 2 : 0) |
-                        (j0 + kPTile > nraw ? 4 : 0);
-      switch (touch) {
-        case 1: mask_tile<true, false, false>(s, tr); break;
-        case 2: mask_tile<false, true, false>(s, tr); break;
-        case 3: mask_tile<true, true, false>(s, tr); break;
-        case 4: mask_tile<false, false, true>(s, tr); break;
-        case 6: mask_tile<false, true, true>(s, tr); break;
-        default: mask_tile<true, true, true>(s, tr); break;
-      }
-    }
+    if (seen == kSeenSome) mask_scores(s, kl, j0, half, tq[0], wlo[0], nvis[0]);
     float tmax = s[0][0];
 #pragma unroll
     for (int h = 0; h < kPSub; ++h)

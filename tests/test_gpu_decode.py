@@ -2,7 +2,8 @@
 
 Covers: the device key resolver (bit-exact), raw append and ring placement (bit-exact),
 the tiny fp32 draft layer over a 240-step decode loop crossing slot boundaries, a
-Llama-3.2-3B-shaped bf16 layer at edge positions up to t = 8192, the full-KV baseline,
+Llama-3.2-3B-shaped bf16 layer at edge positions up to t = 8192, the full-KV baseline
+(including split plans up to 128 work-groups per sequence and KV head),
 bitwise equality MASW == full-KV while t <= S + W, one-hot support, device error bits
 and run-to-run determinism.
 """
@@ -202,6 +203,34 @@ def test_fullkv_decode(dtype):
         ref = O.fullkv_decode(qn[b], kn[b], vn[b], t, O.default_scale(D))
         assert_close(out[b], ref, dtype, f"full-KV b={b} t={t}")
     assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("splits", [9, 16, 40, 128])
+@pytest.mark.parametrize("G,D,dtype", [(8, 128, torch.bfloat16), (3, 64, torch.float32), (1, 128, torch.bfloat16)])
+def test_fullkv_decode_many_splits(splits, G, D, dtype):
+    """Split plans whose last work-group folds more than one batch of eight partials, and
+    group sizes where a thread of the merge takes more than one output pair (G = 8)."""
+    B, Hkv, N = 2, 2, 6000
+    Hq = G * Hkv
+    ts = [N, 4321]
+    k, v = SI.full_cache(B, Hkv, N, D, seed=15, dtype=dtype)
+    q = SI.normal((B, Hq, D), seed=16, dtype=dtype)
+    d = M.Dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, dtype=dtype, num_splits=splits)
+    seq_len = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.full((B, Hq, D), float("nan"), dtype=dtype, device=DEV)
+    ws = M.workspace(d, M.OP_FULLKV_DECODE, max_keys=N, device=DEV)
+    kd, vd, qd = k.to(DEV), v.to(DEV), q.to(DEV)
+    M.fullkv_decode_attn(d, kd, vd, seq_len, err, qd, out, ws)
+    kn, vn, qn = np_in(k), np_in(v), np_in(q).astype(np.float64)
+    for b, t in enumerate(ts):
+        ref = O.fullkv_decode(qn[b], kn[b], vn[b], t, O.default_scale(D))
+        assert_close(out[b], ref, dtype, f"full-KV b={b} t={t} splits={splits}")
+    assert int(err.item()) == 0
+    # the tickets are back at zero: a second call gives the same bits
+    out2 = torch.full_like(out, float("nan"))
+    M.fullkv_decode_attn(d, kd, vd, seq_len, err, qd, out2, ws)
+    assert torch.equal(out, out2)
 
 
 @pytest.mark.parametrize("splits", [1, 4, 7])

@@ -68,6 +68,7 @@ constexpr int kPWaves = 4;
 constexpr int kStepK = 32;         // hidden rows per MFMA step
 constexpr int kPF = 4;             // steps whose weight loads a wave keeps in flight together
 constexpr int kTRow = kStepK + 8;  // transposed tile row (bf16), padded: 80 bytes
+constexpr int kPrefillRowGroups = 4;   // groups of 16 H rows per work-group in a prefill
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -94,22 +95,26 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// grid = (N / 64 column blocks, 2 matrices, ksplits x groups of 16 rows of H: the
-// sequences at a boundary, or the (sequence, slot) pairs of a prefill).  A
-// work-group reduces hidden rows [ks * k_per_split, +k_per_split) of its 64 columns;
-// each of its 4 waves takes a contiguous quarter, keeps kPF steps of weight loads in
-// flight, transposes each [32 k][64 n] tile through its own LDS tile and feeds four
-// v_mfma_f32_16x16x32_bf16 (A = H rows, zero-padded to 16; B = the transposed tile).
+// grid = (N / 64 column blocks, 2 matrices, ksplits x groups of 16 RG rows of H: the
+// sequences at a boundary (RG = 1), or the (sequence, slot) pairs of a prefill
+// (RG = kPrefillRowGroups)).  A work-group reduces hidden rows
+// [ks * k_per_split, +k_per_split) of its 64 columns; each of its 4 waves takes a
+// contiguous quarter, keeps kPF steps of weight loads in flight, transposes each
+// [32 k][64 n] tile through its own LDS tile and feeds, for each of its RG groups of 16
+// rows, four v_mfma_f32_16x16x32_bf16 (A = H rows, zero-padded; B = the transposed
+// tile), so every weight tile read serves 16 RG rows.
 // Waves are summed in LDS in a fixed order; with several hidden splits the
 // last-arriving work-group of the column block adds the split partials in split order
 // (the ticket protocol of the decode merge), so the result is deterministic.
+template <int RG>
 __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const ProjectArgs a) {
+  constexpr int kRows = 16 * RG;   // rows of H per work-group
   const int nblk = blockIdx.x, which = blockIdx.y;
   const int bg = blockIdx.z / a.ksplits, ks = blockIdx.z - (blockIdx.z / a.ksplits) * a.ksplits;
   const int N = a.Hkv * a.D;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
-  __shared__ int sm_m[16], sm_b[16];
+  __shared__ int sm_m[kRows], sm_b[kRows];
   __shared__ int sm_any, sm_last;
   __shared__ __attribute__((aligned(16))) float red[kPWaves * 16 * kCols];
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kPWaves * kCols * kTRow];
@@ -118,8 +123,8 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
   const int rows = a.prefill_ns > 0 ? a.B * a.prefill_ns : a.B;
   if (tid == 0) sm_any = 0;
   __syncthreads();
-  if (tid < 16) {
-    const int row = bg * 16 + tid;
+  if (tid < kRows) {
+    const int row = bg * kRows + tid;
     int bits = 0, m = 0, b = row;
     if (a.prefill_ns > 0) {
       if (row < rows) m = prefill_slot(a, row, nblk == 0 && which == 0 && ks == 0, b, bits);
@@ -141,19 +146,21 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
   const int k_wave = a.k_per_split / kPWaves;                 // hidden rows of this wave
   const int kw0 = ks * a.k_per_split + wave * k_wave;
   const int n_steps = k_wave / kStepK;
-  const int brow = bg * 16 + (lane & 15);
+  const int brow = bg * kRows + (lane & 15);   // + 16 rg
   const int col8 = lane & 7, kq = lane >> 3;   // loader: 8 lanes per 128-byte row segment
   const bool rope = a.rope_theta > 0.f;
   const bool pair_halves = rope && a.rope_style == 0 && which == 0;   // K only; V keeps whole 128-byte rows
   const int wcol = proj_col(nblk, col8 * 8, a.D, pair_halves);   // 8 columns never straddle 32
 
-  f32x4_t acc[4];
+  f32x4_t acc[RG][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[rg][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int s0 = 0; s0 < n_steps; s0 += kPF) {
     u32x4_t wv[kPF][4];
-    u32x4_t av[kPF];
+    u32x4_t av[kPF][RG];
 #pragma unroll
     for (int p = 0; p < kPF; ++p) {
       const int kk = kw0 + (s0 + p) * kStepK;
@@ -166,9 +173,11 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
                        : u32x4_t{0, 0, 0, 0};
       }
       const int ka = kk + (lane >> 4) * 8;
-      av[p] = on && brow < rows && ka < a.hidden
-                  ? *reinterpret_cast<const u32x4_t*>(H + size_t(brow) * a.hidden + ka)
-                  : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+        av[p][rg] = on && brow + 16 * rg < rows && ka < a.hidden
+                        ? *reinterpret_cast<const u32x4_t*>(H + size_t(brow + 16 * rg) * a.hidden + ka)
+                        : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int p = 0; p < kPF; ++p) {
@@ -185,70 +194,80 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(wt + (nt * 16 + (lane & 15)) * kTRow + (lane >> 4) * 8);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[p]),
-                                                          __builtin_bit_cast(bf16x8_t, bv), acc[nt], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          acc[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[p][rg]),
+                                                                __builtin_bit_cast(bf16x8_t, bv), acc[rg][nt], 0, 0, 0);
       }
     }
   }
 
-  // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16)+i of column lane%16.
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      red[(wave * 16 + (lane >> 4) * 4 + i) * kCols + nt * 16 + (lane & 15)] = acc[nt][i];
-  __syncthreads();
-  constexpr int kOut = 16 * kCols / (kPWaves * kWave);   // outputs per thread
-  float s[kOut];
-#pragma unroll
-  for (int j = 0; j < kOut; ++j) {
-    const int idx = tid + j * kPWaves * kWave;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kPWaves; ++w) v += red[w * 16 * kCols + idx];
-    s[j] = v;
-  }
-  uint16_t* dst = static_cast<uint16_t*>(which ? a.v_slot : a.k_slot);
-  if (a.ksplits > 1) {
-    // publish this split's partial; the last split of the column block adds them up
-    float* part = a.part + (size_t(bg * 2 + which) * a.ksplits) * 16 * N;
-#pragma unroll
-    for (int j = 0; j < kOut; ++j) {
-      const int idx = tid + j * kPWaves * kWave;
-      store_partial(&part[size_t(ks) * 16 * N + (idx / kCols) * N + nblk * kCols + idx % kCols], s[j]);
-    }
-    int32_t* cnt = a.counters + (bg * 2 + which) * (N / kCols) + nblk;
-    if (!split_arrive(cnt, a.ksplits, &sm_last)) return;
-#pragma unroll
-    for (int j = 0; j < kOut; ++j) {
-      const int idx = tid + j * kPWaves * kWave;
-      const float* pp = part + (idx / kCols) * N + nblk * kCols + idx % kCols;
-      float v[kMaxProjectSplits];
-#pragma unroll
-      for (int q = 0; q < kMaxProjectSplits; ++q) v[q] = q < a.ksplits ? load_partial(&pp[size_t(q) * 16 * N]) : 0.f;
-      float t = 0.f;
-#pragma unroll
-      for (int q = 0; q < kMaxProjectSplits; ++q) t += v[q];   // split order; absent splits add 0
-      s[j] = t;
-    }
-    if (tid == 0) reset_ticket(cnt);
-  }
-  // thread tid holds local column tid % 64 (its lane) of rows tid / 64 + 4 j
+  // Rows 16 rg .. 16 rg + 15 in turn: the waves' sums meet in LDS, then each thread
+  // finishes (split sum, rotation, rounding) its column of four rows.
   const int n = proj_col(nblk, tid % kCols, a.D, pair_halves);
   const int kvh = n / a.D, d = n - (n / a.D) * a.D;
   const double inv_freq = rope && which == 0 ? rope_inv_freq(rope_freq(d, a.rope_style, a.D), a.D, a.rope_theta) : 0.0;
+  uint16_t* dst = static_cast<uint16_t*>(which ? a.v_slot : a.k_slot);
+  constexpr int kOut = 16 * kCols / (kPWaves * kWave);   // outputs per thread
 #pragma unroll
-  for (int j = 0; j < kOut; ++j) {
-    const int idx = tid + j * kPWaves * kWave;
-    const int row = idx / kCols;
-    const int b = sm_b[row];
-    const int m = sm_m[row];
-    float x = s[j];
-    if (rope && which == 0) {   // uniform: every lane takes part in the exchange
-      const float xp = __shfl_xor(x, a.rope_style == 0 ? 32 : 1, kWave);
-      if (m > 0) x = rope_turn(x, xp, rope_first(d, a.rope_style, a.D), inv_freq, a.g.S + m * a.g.r);
+  for (int rg = 0; rg < RG; ++rg) {
+    if (rg > 0) __syncthreads();   // the previous group's sums are read
+    // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16)+i of column lane%16.
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(wave * 16 + (lane >> 4) * 4 + i) * kCols + nt * 16 + (lane & 15)] = acc[rg][nt][i];
+    __syncthreads();
+    float s[kOut];
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int idx = tid + j * kPWaves * kWave;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kPWaves; ++w) v += red[w * 16 * kCols + idx];
+      s[j] = v;
     }
-    if (m > 0) dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = f32_to_bf16(x);
+    if constexpr (RG == 1) {
+      if (a.ksplits > 1) {
+        // publish this split's partial; the last split of the column block adds them up
+        float* part = a.part + (size_t(bg * 2 + which) * a.ksplits) * 16 * N;
+#pragma unroll
+        for (int j = 0; j < kOut; ++j) {
+          const int idx = tid + j * kPWaves * kWave;
+          store_partial(&part[size_t(ks) * 16 * N + (idx / kCols) * N + nblk * kCols + idx % kCols], s[j]);
+        }
+        int32_t* cnt = a.counters + (bg * 2 + which) * (N / kCols) + nblk;
+        if (!split_arrive(cnt, a.ksplits, &sm_last)) return;
+#pragma unroll
+        for (int j = 0; j < kOut; ++j) {
+          const int idx = tid + j * kPWaves * kWave;
+          const float* pp = part + (idx / kCols) * N + nblk * kCols + idx % kCols;
+          float v[kMaxProjectSplits];
+#pragma unroll
+          for (int q = 0; q < kMaxProjectSplits; ++q) v[q] = q < a.ksplits ? load_partial(&pp[size_t(q) * 16 * N]) : 0.f;
+          float t = 0.f;
+#pragma unroll
+          for (int q = 0; q < kMaxProjectSplits; ++q) t += v[q];   // split order; absent splits add 0
+          s[j] = t;
+        }
+        if (tid == 0) reset_ticket(cnt);
+      }
+    }
+    // thread tid holds local column tid % 64 (its lane) of rows tid / 64 + 4 j
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int idx = tid + j * kPWaves * kWave;
+      const int row = rg * 16 + idx / kCols;
+      const int b = sm_b[row];
+      const int m = sm_m[row];
+      float x = s[j];
+      if (rope && which == 0) {   // uniform: every lane takes part in the exchange
+        const float xp = __shfl_xor(x, a.rope_style == 0 ? 32 : 1, kWave);
+        if (m > 0) x = rope_turn(x, xp, rope_first(d, a.rope_style, a.D), inv_freq, a.g.S + m * a.g.r);
+      }
+      if (m > 0) dst[((size_t(b) * a.Hkv + kvh) * a.g.max_slots + (m - 1)) * a.D + d] = f32_to_bf16(x);
+    }
   }
 }
 
@@ -295,10 +314,15 @@ int launch_project(const ProjectArgs& a, int dtype, hipStream_t s) {
   const int N = a.Hkv * a.D;
   if (dtype == MASW_BF16) {
     if (a.ksplits < 1 || a.ksplits > kMaxProjectSplits || a.k_per_split % (kPWaves * kStepK)) return MASW_ERR_ARG;
-    const long rows = a.prefill_ns > 0 ? long(a.B) * a.prefill_ns : long(a.B);
-    if (a.prefill_ns > 0 && a.ksplits != 1) return MASW_ERR_ARG;
-    hipLaunchKernelGGL(project_mfma_kernel, dim3(N / kCols, 2, a.ksplits * ((rows + 15) / 16)),
-                       dim3(kPWaves * kWave), 0, s, a);
+    if (a.prefill_ns > 0) {
+      if (a.ksplits != 1) return MASW_ERR_ARG;
+      const long rows = long(a.B) * a.prefill_ns, per = 16 * kPrefillRowGroups;
+      hipLaunchKernelGGL(project_mfma_kernel<kPrefillRowGroups>, dim3(N / kCols, 2, (rows + per - 1) / per),
+                         dim3(kPWaves * kWave), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(project_mfma_kernel<1>, dim3(N / kCols, 2, a.ksplits * ((a.B + 15) / 16)), dim3(kPWaves * kWave), 0,
+                         s, a);
+    }
   } else {
     if (a.prefill_ns > 0) return MASW_ERR_UNIMPLEMENTED;
     hipLaunchKernelGGL(project_valu_kernel<float>, dim3((2 * N + 255) / 256, a.B), dim3(256), 0, s, a);

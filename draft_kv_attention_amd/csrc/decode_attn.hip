@@ -8,8 +8,9 @@
 // Work decomposition (CDNA4, wave64):
 //   grid  = (splits, Hkv, B); each work-group owns one contiguous chunk of the logical
 //           key list of one (sequence, KV head); each of its 4 waves streams an equal
-//           contiguous quarter of the chunk in tiles of TK keys (decode_tile_keys), optionally
-//           double-buffered (tile i+1 in flight while tile i is reduced).
+//           contiguous quarter of the chunk in tiles of TK keys (decode_tile_keys), two
+//           tiles in flight as asynchronous global->LDS copies while it reduces the
+//           previous one (register-staged variants remain behind build switches).
 //   wave  = 64/LPR rows of LPR lanes; a row holds one key.  bf16: 8 lanes x 32 bytes
 //           per 256-byte row (D = 128), so a load instruction pair moves 8 whole rows;
 //           q.k partial dots use v_dot2_f32_bf16 and are summed over the 8 lanes with
@@ -17,11 +18,11 @@
 //           rows (one v_perm_b32 per dword) and P is rounded to bf16 for that product,
 //           the usual flash-attention precision; the running sum l stays fp32.
 //           fp32 (small models): 16 lanes per row and plain FMAs.
-//   softmax is online (running max in log2 units, rescale per tile); waves merge
-//   through LDS; splits merge in the same launch: every work-group writes an
-//   (max, sum, o) partial and the last one to finish its (sequence, KV head) - found
-//   with an atomic ticket, reset to zero afterwards - merges them (flash-decoding
-//   without a second kernel).
+//   softmax is online (running max in log2 units, rescale per tile); each wave sums
+//   its row groups as a reduce-scatter and the waves merge through LDS; splits merge
+//   in the same launch: every work-group writes an (max, sum, o) partial and the last
+//   one to finish its (sequence, KV head) - found with an atomic ticket, reset to zero
+//   afterwards - merges them (flash-decoding without a second kernel).
 // Every key row is located through resolve_key(), which maps the logical index to
 // sink row i-1, ring row (i-S-1) mod (W+r) or slot row m-1 on the device, so no host
 // round trip is needed when t changes.  With a fused append the newest n_new raw

@@ -82,11 +82,13 @@ __device__ __forceinline__ size_t verify_prow(const VerifyArgs& a, int b, int kv
 }
 
 // Combine n_valid (max, sum, o) partials of the R rows of one KV head into out.
-// Phase 1: one thread per row loads every split's (max, sum) and leaves the normalized
-// split weights exp2(m_s - M) / L in sm_w ([R][n_valid] floats of LDS the caller no
-// longer needs).  Phase 2: thread t owns column d = t % 128 of the rows t / 128,
-// t / 128 + 2, ...; it issues the o loads of kRowBatch rows x kSplitBatch splits
-// together and accumulates in registers, so the merge costs a few round trips.
+// Phase 1: one thread per row loads its splits' (max, sum) pairs as 8-byte words (a
+// batch of kSplitBatch splits per round trip), folds them online and leaves the
+// normalized split weights exp2(m_s - M) / L in sm_w ([R][n_valid] floats of LDS the
+// caller no longer needs).  Phase 2: thread t owns the column pair 2 (t % 64), +1 of
+// rows t / 64, t / 64 + 4, ...; it issues the 8-byte o loads of kRowBatch rows x
+// kSplitBatch splits together and accumulates in registers, so 32 rows of up to eight
+// splits cost one round trip.
 static_assert(kMaxVerifySplits * kMaxRows * 4 <= 32 * 1024, "split weights fit in the tile buffers");
 __device__ __forceinline__ void merge_verify_partials(const VerifyArgs& a, int b, int kvh, int R, int n_valid,
                                                       float* sm_w) {
@@ -96,50 +98,45 @@ __device__ __forceinline__ void merge_verify_partials(const VerifyArgs& a, int b
   if (threadIdx.x < R) {
     const float* ml = a.part_ml + verify_prow(a, b, kvh, threadIdx.x) * a.n_splits * 2;
     float* w_row = sm_w + threadIdx.x * n_valid;
-    float M = -INFINITY;
+    float M = -INFINITY, L = 0.f;
     for (int s0 = 0; s0 < n_valid; s0 += kSplitBatch) {
-      float mm[kSplitBatch];
+      float2 p[kSplitBatch];
 #pragma unroll
-      for (int k = 0; k < kSplitBatch; ++k) mm[k] = s0 + k < n_valid ? load_partial(&ml[2 * (s0 + k)]) : -INFINITY;
+      for (int k = 0; k < kSplitBatch; ++k)
+        p[k] = s0 + k < n_valid ? load_partial2(&ml[2 * (s0 + k)]) : make_float2(-INFINITY, 0.f);
+      float mb = M;
 #pragma unroll
-      for (int k = 0; k < kSplitBatch; ++k) M = fmaxf(M, mm[k]);
+      for (int k = 0; k < kSplitBatch; ++k) mb = fmaxf(mb, p[k].x);
+      const float mbr = mb == -INFINITY ? 0.f : mb;   // splits past a row's causal limit carry -inf
+      L *= fast_exp2(M - mbr);
+#pragma unroll
+      for (int k = 0; k < kSplitBatch; ++k) {
+        L = fmaf(fast_exp2(p[k].x - mbr), p[k].y, L);
+        if (s0 + k < n_valid) w_row[s0 + k] = p[k].x;
+      }
+      M = mb;
     }
     const float Mr = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
-    for (int s0 = 0; s0 < n_valid; s0 += kSplitBatch) {
-      float mm[kSplitBatch], ll[kSplitBatch];
-#pragma unroll
-      for (int k = 0; k < kSplitBatch; ++k) {
-        const bool in = s0 + k < n_valid;
-        mm[k] = in ? load_partial(&ml[2 * (s0 + k)]) : -INFINITY;
-        ll[k] = in ? load_partial(&ml[2 * (s0 + k) + 1]) : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < kSplitBatch; ++k) {
-        const float w = fast_exp2(mm[k] - Mr);   // splits past a row's causal limit carry -inf
-        L = fmaf(w, ll[k], L);
-        if (s0 + k < n_valid) w_row[s0 + k] = w;
-      }
-    }
     const float inv = 1.f / L;
-    for (int sp = 0; sp < n_valid; ++sp) w_row[sp] *= inv;
+    for (int sp = 0; sp < n_valid; ++sp) w_row[sp] = fast_exp2(w_row[sp] - Mr) * inv;
   }
   __syncthreads();
-  const int d = threadIdx.x % kD, r0 = threadIdx.x / kD;
-  constexpr int kRowStep = kVThreads / kD;
+  constexpr int kPairs = kD / 2;
+  constexpr int kRowStep = kVThreads / kPairs;
+  const int dp = 2 * (threadIdx.x % kPairs), r0 = threadIdx.x / kPairs;
   for (int rb = r0; rb < R; rb += kRowStep * kRowBatch) {
-    float O[kRowBatch];
+    float2 O[kRowBatch];
 #pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) O[i] = 0.f;
+    for (int i = 0; i < kRowBatch; ++i) O[i] = make_float2(0.f, 0.f);
     for (int s0 = 0; s0 < n_valid; s0 += kSplitBatch) {
-      float v[kRowBatch][kSplitBatch];
+      float2 v[kRowBatch][kSplitBatch];
 #pragma unroll
       for (int i = 0; i < kRowBatch; ++i) {
         const int row = rb + i * kRowStep;
-        const float* po = a.part_o + verify_prow(a, b, kvh, row < R ? row : r0) * a.n_splits * kD + d;
+        const float* po = a.part_o + verify_prow(a, b, kvh, row < R ? row : r0) * a.n_splits * kD + dp;
 #pragma unroll
         for (int k = 0; k < kSplitBatch; ++k)
-          v[i][k] = row < R && s0 + k < n_valid ? load_partial(&po[size_t(s0 + k) * kD]) : 0.f;
+          v[i][k] = row < R && s0 + k < n_valid ? load_partial2(&po[size_t(s0 + k) * kD]) : make_float2(0.f, 0.f);
       }
 #pragma unroll
       for (int i = 0; i < kRowBatch; ++i) {
@@ -147,13 +144,19 @@ __device__ __forceinline__ void merge_verify_partials(const VerifyArgs& a, int b
         if (row >= R) continue;
 #pragma unroll
         for (int k = 0; k < kSplitBatch; ++k)
-          if (s0 + k < n_valid) O[i] = fmaf(sm_w[row * n_valid + s0 + k], v[i][k], O[i]);
+          if (s0 + k < n_valid) {
+            const float w = sm_w[row * n_valid + s0 + k];
+            O[i].x = fmaf(w, v[i][k].x, O[i].x);
+            O[i].y = fmaf(w, v[i][k].y, O[i].y);
+          }
       }
     }
 #pragma unroll
     for (int i = 0; i < kRowBatch; ++i) {
       const int row = rb + i * kRowStep;
-      if (row < R) out[verify_prow(a, b, kvh, row) * kD + d] = f32_to_bf16(O[i]);
+      if (row < R)
+        *reinterpret_cast<uint32_t*>(out + verify_prow(a, b, kvh, row) * kD + dp) =
+            uint32_t(f32_to_bf16(O[i].x)) | (uint32_t(f32_to_bf16(O[i].y)) << 16);
     }
   }
 }
@@ -593,27 +596,31 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
   }
   __syncthreads();
 
+  // Each thread combines the waves for two adjacent columns of a row.
   uint16_t* out = static_cast<uint16_t*>(a.out);
-  for (int idx = threadIdx.x; idx < R * kD; idx += kVThreads) {
-    const int row = idx / kD, d = idx - (idx / kD) * kD;
+  for (int pi = threadIdx.x; pi < R * kD / 2; pi += kVThreads) {
+    const int row = 2 * pi / kD, d = 2 * pi - row * kD;
     const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
     const size_t prow = (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
     float Mr = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kVWaves; ++w) Mr = fmaxf(Mr, sm_ml[w][row][0]);
     const float Mrr = Mr == -INFINITY ? 0.f : Mr;
-    float L = 0.f, O = 0.f;
+    float L = 0.f, O0 = 0.f, O1 = 0.f;
 #pragma unroll
     for (int w = 0; w < kVWaves; ++w) {
       L = fmaf(fast_exp2(sm_ml[w][row][0] - Mrr), sm_ml[w][row][1], L);
-      O += sm_o[(w * NB * 32 + row) * kD + d];
+      const float2 o2 = *reinterpret_cast<const float2*>(&sm_o[(w * NB * 32 + row) * kD + d]);
+      O0 += o2.x;
+      O1 += o2.y;
     }
     if (n_valid == 1) {
-      out[prow * kD + d] = f32_to_bf16(O / L);
+      *reinterpret_cast<uint32_t*>(out + prow * kD + d) =
+          uint32_t(f32_to_bf16(O0 / L)) | (uint32_t(f32_to_bf16(O1 / L)) << 16);
     } else {
       const size_t pr = prow * a.n_splits + split;
-      store_partial(&a.part_o[pr * kD + d], O);
-      if (d == 0) { store_partial(&a.part_ml[pr * 2], Mr); store_partial(&a.part_ml[pr * 2 + 1], L); }
+      store_partial2(&a.part_o[pr * kD + d], O0, O1);
+      if (d == 0) store_partial2(&a.part_ml[pr * 2], Mr, L);
     }
   }
   if (n_valid == 1) return;

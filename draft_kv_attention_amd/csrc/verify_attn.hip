@@ -21,7 +21,7 @@
 // w / (4/NB) and the 32-key slice w % (4/NB) of the tile, so each wave keeps one 64-float
 // O^T accumulator.  The next tile's global loads are issued into registers before the
 // current tile is computed.  Waves sharing a row block merge through LDS in a fixed
-// order; splits merge in the same launch through the last-arriving work-group.
+// order; the splits are merged by a combine pass launched right after (verify_combine_kernel).
 #include "masw_internal.hpp"
 
 namespace masw {
@@ -81,86 +81,6 @@ __device__ __forceinline__ size_t verify_prow(const VerifyArgs& a, int b, int kv
   return (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
 }
 
-// Combine n_valid (max, sum, o) partials of the R rows of one KV head into out.
-// Phase 1: one thread per row loads its splits' (max, sum) pairs as 8-byte words (a
-// batch of kSplitBatch splits per round trip), folds them online and leaves the
-// normalized split weights exp2(m_s - M) / L in sm_w ([R][n_valid] floats of LDS the
-// caller no longer needs).  Phase 2: thread t owns the column pair 2 (t % 64), +1 of
-// rows t / 64, t / 64 + 4, ...; it issues the 8-byte o loads of kRowBatch rows x
-// kSplitBatch splits together and accumulates in registers, so 32 rows of up to eight
-// splits cost one round trip.
-static_assert(kMaxVerifySplits * kMaxRows * 4 <= 32 * 1024, "split weights fit in the tile buffers");
-__device__ __forceinline__ void merge_verify_partials(const VerifyArgs& a, int b, int kvh, int R, int n_valid,
-                                                      float* sm_w) {
-  constexpr int kRowBatch = 8;
-  constexpr int kSplitBatch = 8;
-  uint16_t* out = static_cast<uint16_t*>(a.out);
-  if (threadIdx.x < R) {
-    const float* ml = a.part_ml + verify_prow(a, b, kvh, threadIdx.x) * a.n_splits * 2;
-    float* w_row = sm_w + threadIdx.x * n_valid;
-    float M = -INFINITY, L = 0.f;
-    for (int s0 = 0; s0 < n_valid; s0 += kSplitBatch) {
-      float2 p[kSplitBatch];
-#pragma unroll
-      for (int k = 0; k < kSplitBatch; ++k)
-        p[k] = s0 + k < n_valid ? load_partial2(&ml[2 * (s0 + k)]) : make_float2(-INFINITY, 0.f);
-      float mb = M;
-#pragma unroll
-      for (int k = 0; k < kSplitBatch; ++k) mb = fmaxf(mb, p[k].x);
-      const float mbr = mb == -INFINITY ? 0.f : mb;   // splits past a row's causal limit carry -inf
-      L *= fast_exp2(M - mbr);
-#pragma unroll
-      for (int k = 0; k < kSplitBatch; ++k) {
-        L = fmaf(fast_exp2(p[k].x - mbr), p[k].y, L);
-        if (s0 + k < n_valid) w_row[s0 + k] = p[k].x;
-      }
-      M = mb;
-    }
-    const float Mr = M == -INFINITY ? 0.f : M;
-    const float inv = 1.f / L;
-    for (int sp = 0; sp < n_valid; ++sp) w_row[sp] = fast_exp2(w_row[sp] - Mr) * inv;
-  }
-  __syncthreads();
-  constexpr int kPairs = kD / 2;
-  constexpr int kRowStep = kVThreads / kPairs;
-  const int dp = 2 * (threadIdx.x % kPairs), r0 = threadIdx.x / kPairs;
-  for (int rb = r0; rb < R; rb += kRowStep * kRowBatch) {
-    float2 O[kRowBatch];
-#pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) O[i] = make_float2(0.f, 0.f);
-    for (int s0 = 0; s0 < n_valid; s0 += kSplitBatch) {
-      float2 v[kRowBatch][kSplitBatch];
-#pragma unroll
-      for (int i = 0; i < kRowBatch; ++i) {
-        const int row = rb + i * kRowStep;
-        const float* po = a.part_o + verify_prow(a, b, kvh, row < R ? row : r0) * a.n_splits * kD + dp;
-#pragma unroll
-        for (int k = 0; k < kSplitBatch; ++k)
-          v[i][k] = row < R && s0 + k < n_valid ? load_partial2(&po[size_t(s0 + k) * kD]) : make_float2(0.f, 0.f);
-      }
-#pragma unroll
-      for (int i = 0; i < kRowBatch; ++i) {
-        const int row = rb + i * kRowStep;
-        if (row >= R) continue;
-#pragma unroll
-        for (int k = 0; k < kSplitBatch; ++k)
-          if (s0 + k < n_valid) {
-            const float w = sm_w[row * n_valid + s0 + k];
-            O[i].x = fmaf(w, v[i][k].x, O[i].x);
-            O[i].y = fmaf(w, v[i][k].y, O[i].y);
-          }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int row = rb + i * kRowStep;
-      if (row < R)
-        *reinterpret_cast<uint32_t*>(out + verify_prow(a, b, kvh, row) * kD + dp) =
-            uint32_t(f32_to_bf16(O[i].x)) | (uint32_t(f32_to_bf16(O[i].y)) << 16);
-    }
-  }
-}
-
 template <int NB>
 __global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyArgs a) {
   constexpr int WPR = VTile<NB>::WPR;
@@ -176,7 +96,6 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t sQ[NB * 32 * kRS];
   __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * TK * kRS];
-  __shared__ int sm_last;
   uint16_t* Kt = sKV;
   uint16_t* Vt = sKV + TK * kRS;
 
@@ -337,14 +256,6 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyArgs a) {
       if (d == 0) { store_partial(&a.part_ml[pr * 2], Mr); store_partial(&a.part_ml[pr * 2 + 1], L); }
     }
   }
-  if (n_valid == 1) return;
-#if MASW_SPLIT_MERGE != 0
-  if (!split_arrive(&a.counters[unit], n_valid, &sm_last)) return;
-  merge_verify_partials(a, b, kvh, R, n_valid, reinterpret_cast<float*>(sKV));
-  if (threadIdx.x == 0) reset_ticket(&a.counters[unit]);
-#else
-  (void)sm_last;
-#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -390,7 +301,6 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
 
   __shared__ u32x4_t vpipe[kVWaves][2][kVStageU4];   // 128 KB; reused by the wave merge
   __shared__ float sm_ml[kVWaves][NB * 32][2];
-  __shared__ int sm_last;
 
   const int t = a.seq_len[b];
   // Q^T operand (B of S^T = K Q^T): lane holds row rb*32 + l32, d = 16 ks + 8 half .. +7.
@@ -623,36 +533,55 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
       if (d == 0) store_partial2(&a.part_ml[pr * 2], Mr, L);
     }
   }
-  if (n_valid == 1) return;
-#if MASW_SPLIT_MERGE != 0
-  if (!split_arrive(&a.counters[unit], n_valid, &sm_last)) return;
-  merge_verify_partials(a, b, kvh, R, n_valid, reinterpret_cast<float*>(&vpipe[0][0][0]));
-  if (threadIdx.x == 0) reset_ticket(&a.counters[unit]);
-#else
-  (void)sm_last;
-#endif
 }
 
-// Separate merge pass (MASW_SPLIT_MERGE 0): one work-group per (row, sequence).
-__global__ __launch_bounds__(kD) void verify_combine_kernel(const VerifyArgs a, int tk) {
-  const int r = blockIdx.x, b = blockIdx.y, d = threadIdx.x;   // r = j * Hq + h
+// Split merge of the verifier, a pass of its own after the attention kernel (the whole
+// GPU combines the partials; merging them in the last work-group of each (sequence, KV
+// head) left one CU pulling 128-256 KB).  64 threads combine one (query row, sequence),
+// two columns each, with the 8-byte loads of a batch of kSplitBatch splits in flight,
+// folded online.
+constexpr int kCombRows = 4;   // query rows per work-group
+__global__ __launch_bounds__(kCombRows * 64) void verify_combine_kernel(const VerifyArgs a, int tk) {
+  constexpr int kSplitBatch = 8;
+  const int r = blockIdx.x * kCombRows + (threadIdx.x >> 6), b = blockIdx.y;   // r = j * Hq + h
+  const int dp = 2 * (threadIdx.x & 63);
+  if (r >= a.n_q * a.Hq) return;
   const int t = a.seq_len[b];
   if (t < a.n_q || t > a.max_len) return;
   const int chunk = verify_chunk(t, a.n_splits, tk);
   const int nv = (t + chunk - 1) / chunk;
-  if (nv == 1) return;
+  if (nv == 1) return;   // written directly by the single work-group
   const size_t prow = size_t(b) * a.n_q * a.Hq + r;
   const float* ml = a.part_ml + prow * a.n_splits * 2;
-  const float* po = a.part_o + prow * a.n_splits * kD + d;
-  float M = -INFINITY;
-  for (int s = 0; s < nv; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < nv; ++s) {
-    const float w = fast_exp2(ml[2 * s] - M);
-    L = fmaf(w, ml[2 * s + 1], L);
-    O = fmaf(w, po[size_t(s) * kD], O);
+  const float* po = a.part_o + prow * a.n_splits * kD + dp;
+  float M = -INFINITY, L = 0.f, O0 = 0.f, O1 = 0.f;
+  for (int s0 = 0; s0 < nv; s0 += kSplitBatch) {
+    float2 p[kSplitBatch], v[kSplitBatch];
+#pragma unroll
+    for (int k = 0; k < kSplitBatch; ++k) {
+      const bool in = s0 + k < nv;
+      p[k] = in ? *reinterpret_cast<const float2*>(&ml[2 * (s0 + k)]) : make_float2(-INFINITY, 0.f);
+      v[k] = in ? *reinterpret_cast<const float2*>(&po[size_t(s0 + k) * kD]) : make_float2(0.f, 0.f);
+    }
+    float mb = M;
+#pragma unroll
+    for (int k = 0; k < kSplitBatch; ++k) mb = fmaxf(mb, p[k].x);
+    const float mbr = mb == -INFINITY ? 0.f : mb;   // splits past a row's causal limit carry -inf
+    const float alpha = fast_exp2(M - mbr);
+    L *= alpha;
+    O0 *= alpha;
+    O1 *= alpha;
+#pragma unroll
+    for (int k = 0; k < kSplitBatch; ++k) {
+      const float w = fast_exp2(p[k].x - mbr);
+      L = fmaf(w, p[k].y, L);
+      O0 = fmaf(w, v[k].x, O0);
+      O1 = fmaf(w, v[k].y, O1);
+    }
+    M = mb;
   }
-  static_cast<uint16_t*>(a.out)[prow * kD + d] = f32_to_bf16(O / L);
+  *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + prow * kD + dp) =
+      uint32_t(f32_to_bf16(O0 / L)) | (uint32_t(f32_to_bf16(O1 / L)) << 16);
 }
 
 }  // namespace
@@ -678,12 +607,9 @@ int launch_verify_mfma(const VerifyArgs& a, hipStream_t s) {
   } else {
     return MASW_ERR_SHAPE;
   }
-#if MASW_SPLIT_MERGE == 0
   if (a.n_splits > 1)
-    hipLaunchKernelGGL(verify_combine_kernel, dim3(a.n_q * a.Hq, a.B), dim3(kD), 0, s, a, tk);
-#else
-  (void)tk;
-#endif
+    hipLaunchKernelGGL(verify_combine_kernel, dim3((a.n_q * a.Hq + kCombRows - 1) / kCombRows, a.B), dim3(kCombRows * 64),
+                       0, s, a, tk);
   return hipGetLastError() == hipSuccess ? MASW_OK : MASW_ERR_LAUNCH;
 }
 

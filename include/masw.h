@@ -40,8 +40,9 @@
  *    buffer of at least masw_workspace_bytes(...) bytes, 256-byte aligned, that no other
  *    call uses concurrently.  The caller zero-fills it once after allocating it; every
  *    call leaves the ticket counters it uses back at zero, so no later clearing is
- *    needed (the split merge happens in the same launch: the last work-group of each
- *    (sequence, KV head) combines the partials).
+ *    needed (the decode paths merge their splits in the same launch: the last
+ *    work-group of each (sequence, KV head) combines the partials; fullkv_verify_attn
+ *    merges them in a second kernel it enqueues on the same stream).
  */
 #ifndef MASW_H_
 #define MASW_H_

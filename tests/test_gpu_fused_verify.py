@@ -103,8 +103,8 @@ def test_fullkv_decode_step_matches_separate_calls():
 # verifier attention
 # ---------------------------------------------------------------------------
 
-def _verify_case(B, Hq, Hkv, D, n_q, ts, max_len, dtype, seed, check_b=None):
-    d = M.Dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, dtype=dtype)
+def _verify_case(B, Hq, Hkv, D, n_q, ts, max_len, dtype, seed, check_b=None, splits=0):
+    d = M.Dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, dtype=dtype, num_splits=splits)
     k, v = SI.full_cache(B, Hkv, max_len, D, seed=seed, dtype=dtype, device=DEV)
     q = SI.normal((B, n_q, Hq, D), seed + 1, dtype=dtype, device=DEV)
     seq = torch.tensor(ts, dtype=torch.int32, device=DEV)
@@ -143,6 +143,15 @@ def test_verify_ragged_small(Hq, Hkv, n_q):
 def test_verify_vector_alu_shapes(dtype, D, Hq, n_q):
     ts = [n_q, 40, 777]
     _verify_case(len(ts), Hq, 8 if Hq % 8 == 0 else 1, D, n_q, ts, 800, dtype, seed=33)
+
+
+@pytest.mark.parametrize("splits", [3, 12, 33, 64])
+@pytest.mark.parametrize("Hq,n_q", [(32, 6), (64, 8)])
+def test_verify_split_plans(splits, Hq, n_q):
+    """Split plans whose combine pass folds more than one batch of eight partials (up to
+    the MFMA verifier's 64), with causal rows whose last splits see no key."""
+    ts = [n_q, 2100, 5000]
+    _verify_case(len(ts), Hq, 8, 128, n_q, ts, 5010, torch.bfloat16, seed=36, splits=splits)
 
 
 def test_verify_out_of_range():

@@ -68,6 +68,11 @@ constexpr int kPWaves = 4;
 constexpr int kStepK = 32;         // hidden rows per MFMA step
 constexpr int kPF = 4;             // steps whose weight loads a wave keeps in flight together
 constexpr int kTRow = kStepK + 8;  // transposed tile row (bf16), padded: 80 bytes
+// The 8-byte k-quads of transposed row n sit at quad q ^ tq_swz(n) (an even XOR keeps a
+// 16-byte read of quads 2g, 2g + 1 whole): the eight rows 8 apart that one store
+// instruction writes then fall on four bank groups instead of two (2-way instead of
+// 4-way conflicts), and the 16-lane row reads stay conflict-free.
+__device__ __forceinline__ int tq_swz(int n) { return 2 * ((n >> 4) & 3); }
 constexpr int kPrefillRowGroups = 4;   // groups of 16 H rows per work-group in a prefill
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -188,12 +193,13 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
       for (int e = 0; e < 8; ++e) {
         uint32_t x0 = u16_of(wv[p][0], e) | (u16_of(wv[p][1], e) << 16);
         uint32_t x1 = u16_of(wv[p][2], e) | (u16_of(wv[p][3], e) << 16);
-        *reinterpret_cast<uint2*>(wt + (col8 * 8 + e) * kTRow + 4 * kq) = make_uint2(x0, x1);
+        *reinterpret_cast<uint2*>(wt + (col8 * 8 + e) * kTRow + 4 * (kq ^ tq_swz(col8 * 8 + e))) = make_uint2(x0, x1);
       }
       wave_lds_sync();
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(wt + (nt * 16 + (lane & 15)) * kTRow + (lane >> 4) * 8);
+        const int n = nt * 16 + (lane & 15);
+        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(wt + n * kTRow + 4 * ((2 * (lane >> 4)) ^ tq_swz(n)));
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
           acc[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[p][rg]),

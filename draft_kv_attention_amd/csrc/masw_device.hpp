@@ -110,13 +110,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // only after the ticket told it everyone else had arrived.
 //   MASW_SPLIT_MERGE 2: that protocol (default);
 //   MASW_SPLIT_MERGE 1: plain stores/loads with __threadfence() around the ticket;
-//   MASW_SPLIT_MERGE 0: no in-launch merge, a separate combine kernel follows.
+//   MASW_SPLIT_MERGE 0: the decode kernel does not merge in-launch, a separate combine
+//                       kernel follows it; the other in-launch merges (the projection's
+//                       hidden slices) keep the protocol of 2.
 #ifndef MASW_SPLIT_MERGE
 #define MASW_SPLIT_MERGE 2
 #endif
 
 __device__ __forceinline__ void store_partial(float* p, float v) {
-#if MASW_SPLIT_MERGE == 2
+#if MASW_SPLIT_MERGE != 1
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #else
   *p = v;
@@ -124,7 +126,7 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
 }
 
 __device__ __forceinline__ float load_partial(const float* p) {
-#if MASW_SPLIT_MERGE == 2
+#if MASW_SPLIT_MERGE != 1
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #else
   return *p;
@@ -134,7 +136,7 @@ __device__ __forceinline__ float load_partial(const float* p) {
 // Two adjacent partial values (an 8-byte aligned pair) as one 64-bit access.
 __device__ __forceinline__ void store_partial2(float* p, float v0, float v1) {
   const uint64_t w = (uint64_t(__float_as_uint(v1)) << 32) | __float_as_uint(v0);
-#if MASW_SPLIT_MERGE == 2
+#if MASW_SPLIT_MERGE != 1
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #else
   *reinterpret_cast<uint64_t*>(p) = w;
@@ -142,7 +144,7 @@ __device__ __forceinline__ void store_partial2(float* p, float v0, float v1) {
 }
 
 __device__ __forceinline__ float2 load_partial2(const float* p) {
-#if MASW_SPLIT_MERGE == 2
+#if MASW_SPLIT_MERGE != 1
   const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #else
   const uint64_t w = *reinterpret_cast<const uint64_t*>(p);

@@ -540,15 +540,25 @@ def verify_leg(dev, prefix=32768, n_q=6, batch=4):
     return out
 
 
-def materialize_leg(stack, t_boundary, replays=5, dims=None):
+def materialize_leg(stack, t_boundary, replays=5, dims=None, ws=None):
     """One slot boundary across the 28 layers (projection + structured-mask slot query).
 
     Each replay first resets every layer's n_slots to m-1 (so the boundary is pending
     again); a graph holding only those resets is timed separately and subtracted.
-    `dims` overrides the stack's (e.g. to rotate the slot keys).
+    `dims` overrides the stack's (e.g. to rotate the slot keys, or a smaller batch: the
+    first sequences of every tensor), `ws` the workspace (one per plan).
     """
     L = stack.L
     d = dims if dims is not None else stack.d
+    ws = ws if ws is not None else stack.ws
+    B = d.batch
+
+    def sub(x):
+        return x if B == stack.shape.batch else x[:B]
+
+    layers = [M.Layer(**{f.name: sub(getattr(lay, f.name)) for f in dataclasses.fields(lay)})
+              for lay in stack.layers]
+    seq = M.Seq(seq_len=sub(stack.seq.seq_len), err=stack.seq.err)
     stack.set_position(t_boundary)
     m = (t_boundary - stack.S - stack.W) // stack.r
 
@@ -559,8 +569,8 @@ def materialize_leg(stack, t_boundary, replays=5, dims=None):
     def boundary():
         resets()
         for i in range(L):
-            M.masw_materialize_slot(d, stack.layers[i], stack.seq, stack.h[i], stack.wk[i], stack.wv[i],
-                                    stack.qg[i], stack.og[i], stack.ws)
+            M.masw_materialize_slot(d, layers[i], seq, sub(stack.h[i]), stack.wk[i], stack.wv[i],
+                                    sub(stack.qg[i]), sub(stack.og[i]), ws)
 
     times = {}
     for name, fn in (("resets", resets), ("boundary", boundary)):
@@ -584,9 +594,9 @@ def materialize_leg(stack, t_boundary, replays=5, dims=None):
     per_layer = (times["boundary"] - times["resets"]) / L
     sh = stack.shape
     keys = stack.S + stack.W + m - 1
-    nbytes = (2 * sh.hidden * sh.n_kv_heads * sh.head_dim * 2 + sh.batch * sh.hidden * 2
-              + stack.attn_bytes(keys) + sh.batch * stack.kv_row_bytes())
-    return dict(slot_index=m, us_per_layer=round(per_layer, 2), bytes_per_layer=int(nbytes),
+    nbytes = (2 * sh.hidden * sh.n_kv_heads * sh.head_dim * 2 + B * sh.hidden * 2
+              + stack.attn_bytes(keys) * B // sh.batch + B * stack.kv_row_bytes())
+    return dict(batch=B, slot_index=m, us_per_layer=round(per_layer, 2), bytes_per_layer=int(nbytes),
                 gbs=round(nbytes / per_layer / 1e3, 1), per_decode_step_us=round(per_layer * L / stack.r, 2),
                 slots_after=int(stack.layers[0].n_slots[0].item()))
 
@@ -731,6 +741,10 @@ def main():
     mat["rope_us_per_layer"] = mat_rope["us_per_layer"]
     # trend in the number of prior slots (the slot query's key list grows by one per slot)
     mat["us_per_layer_by_slot"] = {m: materialize_leg(stack, 2052 + m * 64)["us_per_layer"] for m in (1, 128, 256, 480)}
+    # the slot-chain workload's own batch of 4 (the first 4 sequences of the stack)
+    d4 = dataclasses.replace(stack.d, batch=4)
+    ws4 = M.workspace(d4, M.OP_MATERIALIZE, device=dev)
+    mat["batch4"] = {m: materialize_leg(stack, 2052 + m * 64, dims=d4, ws=ws4) for m in (1, 480)}
     print(f"[bench] materialization {mat}", file=sys.stderr, flush=True)
     del stack
     torch.cuda.empty_cache()

@@ -196,7 +196,9 @@ def workspace_bytes(d: Dims, op: int, max_keys: int = 0, n_q: int = 0) -> int:
 
 
 def workspace(d: Dims, op: int, max_keys: int = 0, n_q: int = 0, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace (the split tickets must start at zero; calls keep them so)."""
+    """Zero-filled workspace (the split tickets must start at zero; calls keep them so).
+    It serves one plan: share it only between calls with equal Dims (and, for the
+    full-KV ops, equal max_keys / n_q); zero it again before another plan uses it."""
     n = workspace_bytes(d, op, max_keys, n_q)
     if n == 0:
         raise MaswError("masw_workspace_bytes", -1)

@@ -15,13 +15,16 @@
 // layout (lane = row, registers = keys) is the B-operand layout the second product
 // needs, with its 32 keys taken in the order the registers hold them.
 //
-// Work-group = 4 waves over one (split, KV head, sequence).  Per iteration the whole
-// work-group stages a tile of 32*4/NB keys of K and V in LDS (272-byte padded rows:
-// conflict-free 16-byte row reads and 2-byte column reads); wave w owns row block
-// w / (4/NB) and the 32-key slice w % (4/NB) of the tile, so each wave keeps one 64-float
-// O^T accumulator.  The next tile's global loads are issued into registers before the
-// current tile is computed.  Waves sharing a row block merge through LDS in a fixed
-// order; the splits are merged by a combine pass launched right after (verify_combine_kernel).
+// Work-group = 4 waves over one (split, KV head, sequence); two kernels implement it.
+// verify_stream_kernel (the default, further down) lets every wave stream its own key
+// range through private LDS stages.  verify_kernel (MASW_VERIFY_STREAM=0, the earlier
+// design) stages a tile of 32*4/NB keys of K and V per iteration for the whole
+// work-group (272-byte padded rows: conflict-free 16-byte row reads and 2-byte column
+// reads); wave w owns row block w / (4/NB) and the 32-key slice w % (4/NB) of the tile,
+// so each wave keeps one 64-float O^T accumulator, and the next tile's global loads are
+// issued into registers before the current tile is computed.  In both the waves merge
+// through LDS in a fixed order; the splits are merged by a combine pass launched right
+// after (verify_combine_kernel).
 #include "masw_internal.hpp"
 
 namespace masw {

@@ -42,7 +42,13 @@
  *    call leaves the ticket counters it uses back at zero, so no later clearing is
  *    needed (the decode paths merge their splits in the same launch: the last
  *    work-group of each (sequence, KV head) combines the partials; fullkv_verify_attn
- *    merges them in a second kernel it enqueues on the same stream).
+ *    merges them in a second kernel it enqueues on the same stream).  Where counters
+ *    and partials sit depends on the plan, so a workspace serves one plan: calls may
+ *    share it when they pass equal masw_dims (masw_draft_attn, masw_decode_step and
+ *    masw_materialize_slot of one dims share a plan; the full-KV ops also need equal
+ *    max_len, and n_q for the verifier).  Before a call with another plan uses it, the
+ *    caller zero-fills it again, or uses another buffer: otherwise that plan's counters
+ *    may lie where the previous plan left partial sums, and results are wrong.
  */
 #ifndef MASW_H_
 #define MASW_H_

@@ -23,13 +23,15 @@ int check_dims(const masw_dims* d, bool masw_memory) {
   if (!d) return MASW_ERR_ARG;
   if (d->dtype != MASW_F32 && d->dtype != MASW_BF16) return MASW_ERR_DTYPE;
   if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return MASW_ERR_SHAPE;
+  if (d->batch > kMaxGridDim || d->n_kv_heads > kMaxGridDim) return MASW_ERR_SHAPE;
   if (d->n_q_heads % d->n_kv_heads) return MASW_ERR_SHAPE;
   if (!group_supported(d->n_q_heads / d->n_kv_heads)) return MASW_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return MASW_ERR_SHAPE;
   if (d->num_splits < 0 || d->num_splits > kMaxSplits) return MASW_ERR_ARG;
   if (masw_memory) {
     if (d->sink < 0 || d->window < 1 || d->interval < 0 || d->interval > d->window || d->max_slots < 0 ||
-        d->rollback < 0 || d->rollback > kMaxRollback)
+        d->rollback < 0 || d->rollback > kMaxRollback || d->sink > kMaxMemRows || d->window > kMaxMemRows ||
+        d->max_slots > kMaxMemRows)
       return MASW_ERR_ARG;
     if (!(d->rope_theta >= 0.f) || std::isinf(d->rope_theta) ||
         (d->rope_style != MASW_ROPE_ROTATE_HALF && d->rope_style != MASW_ROPE_INTERLEAVED))

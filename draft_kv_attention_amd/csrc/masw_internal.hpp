@@ -32,6 +32,11 @@ int launch_append(const AppendArgs& a, int dtype, hipStream_t s);
 
 // Rollback rows a memory may keep (ring rows are W + r + rollback).
 constexpr int kMaxRollback = 4096;
+// Largest S, W and max_slots: positions and row indices stay far from int32 overflow
+// (S + W + r + rollback and S + m r are formed in 32 bits).
+constexpr int kMaxMemRows = 1 << 28;
+// Largest batch and KV head count: they are grid dimensions (y/z at most 65535).
+constexpr int kMaxGridDim = 65535;
 int launch_rollback(const MemGeom& g, int rollback, const int32_t* seq_len, const int32_t* t_spec,
                     int32_t* n_slots, int32_t* err, int B, hipStream_t s);
 

@@ -99,18 +99,18 @@ typedef enum {
 /* Geometry and memory parameters.  S, W, r and max_slots are ignored by the
  * full-KV entry points. */
 typedef struct {
-  int32_t batch;       /* B >= 1 sequences                                         */
+  int32_t batch;       /* 1 <= B <= 65535 sequences (a grid dimension)              */
   int32_t n_q_heads;   /* Hq; query head h reads KV head h / (Hq/Hkv) (grouped)     */
-  int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0 and Hq/Hkv in {1,2,3,4,6,8}           */
+  int32_t n_kv_heads;  /* Hkv <= 65535; Hq % Hkv == 0 and Hq/Hkv in {1,2,3,4,6,8}  */
   int32_t head_dim;    /* D in {64, 128}                                           */
-  int32_t sink;        /* S >= 0                                                   */
-  int32_t window;      /* W >= 1                                                   */
+  int32_t sink;        /* 0 <= S <= 2^28                                           */
+  int32_t window;      /* 1 <= W <= 2^28                                           */
   int32_t interval;    /* r, 1 <= r <= W; the local ring holds C = W + r rows.
                           r = 0: no slot chain - sinks ++ the exact W-window only
                           (StreamingLLM-style with S > 0, a sliding window with
                           S = 0); the ring holds C = W rows and every append is
                           legal; masw_materialize_slot returns MASW_ERR_ARG        */
-  int32_t max_slots;   /* slot rows allocated per (sequence, KV head), >= 0         */
+  int32_t max_slots;   /* slot rows allocated per (sequence, KV head), 0..2^28      */
   int32_t dtype;       /* masw_dtype of every K/V/q/out/h/w tensor                 */
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(D) ([TR] §2.3 Eq. 2)  */
   int32_t num_splits;  /* split-K plan: 0 = library heuristic, else splits per

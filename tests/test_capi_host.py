@@ -51,7 +51,9 @@ def _dims(**kw):
     (dict(n_q_heads=20), -3), (dict(head_dim=96), -3), (dict(n_q_heads=40, n_kv_heads=8), -3),
     (dict(dtype=7), -2), (dict(num_splits=257), -1), (dict(batch=0), -3),
     (dict(rope_theta=-1.0), -1), (dict(rope_theta=float("nan")), -1), (dict(rope_theta=float("inf")), -1),
-    (dict(rope_theta=10000.0, rope_style=2), -1)])
+    (dict(rope_theta=10000.0, rope_style=2), -1),
+    (dict(window=(1 << 28) + 1), -1), (dict(sink=(1 << 28) + 1), -1), (dict(max_slots=(1 << 28) + 1), -1),
+    (dict(batch=65536), -3), (dict(n_q_heads=65536 * 2, n_kv_heads=65536), -3)])
 def test_invalid_dims_rejected_on_host(lib, kw, status):
     d = _dims(**kw)
     assert lib.masw_draft_attn(ctypes.byref(d), None, None, None, None, None, 0, None) == status

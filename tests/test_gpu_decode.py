@@ -205,10 +205,11 @@ def test_fullkv_decode(dtype):
     assert int(err.item()) == 0
 
 
-@pytest.mark.parametrize("splits", [9, 16, 40, 128])
+@pytest.mark.parametrize("splits", [9, 16, 40, 128, 256])
 @pytest.mark.parametrize("G,D,dtype", [(8, 128, torch.bfloat16), (3, 64, torch.float32), (1, 128, torch.bfloat16)])
 def test_fullkv_decode_many_splits(splits, G, D, dtype):
-    """Split plans whose last work-group folds more than one batch of eight partials, and
+    """Split plans whose last work-group folds more than one batch of eight partials (up to
+    the largest plan, 256, where only the first 188 / 136 work-groups hold keys), and
     group sizes where a thread of the merge takes more than one output pair (G = 8)."""
     B, Hkv, N = 2, 2, 6000
     Hq = G * Hkv

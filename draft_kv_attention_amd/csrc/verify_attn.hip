@@ -293,6 +293,12 @@ __device__ __forceinline__ void verify_issue(u32x4_t* stage, const uint16_t* kba
   }
 }
 
+// Column c of query row `row` in the wave-merge buffer: its 16-byte group (c / 4) is
+// XOR-ed with the row's low 5 bits.  The rows are 512 bytes apart, so without it the
+// 32 rows one accumulator store instruction writes would all land on the same four
+// banks; with it they spread over all of them, and a row's pairs stay adjacent.
+__device__ __forceinline__ int merge_col(int row, int c) { return c ^ ((row & 31) << 2); }
+
 template <int NB>
 __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        sm_o[(wave * NB * 32 + row) * kD + db * 32 + 8 * (v >> 2) + 4 * half + (v & 3)] = wt * o[rb][db][v];
+        sm_o[(wave * NB * 32 + row) * kD + merge_col(row, db * 32 + 8 * (v >> 2) + 4 * half + (v & 3))] = wt * o[rb][db][v];
   }
   __syncthreads();
 
@@ -523,7 +529,7 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
 #pragma unroll
     for (int w = 0; w < kVWaves; ++w) {
       L = fmaf(fast_exp2(sm_ml[w][row][0] - Mrr), sm_ml[w][row][1], L);
-      const float2 o2 = *reinterpret_cast<const float2*>(&sm_o[(w * NB * 32 + row) * kD + d]);
+      const float2 o2 = *reinterpret_cast<const float2*>(&sm_o[(w * NB * 32 + row) * kD + merge_col(row, d)]);
       O0 += o2.x;
       O1 += o2.y;
     }

@@ -425,19 +425,27 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
     st ^= 1;
     const bool interior = tile + kVWaveKeys <= w1 && tile + kVWaveKeys - 1 <= t - a.n_q;
 
+    // Score products of every row block first, the blocks' chains interleaved (each chain
+    // is eight dependent MFMAs; with one wave per SIMD nothing else would fill the gaps).
+    f32x16_t sacc[NB];
 #pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      f32x16_t s;
+    for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = 0.f;
+      for (int v = 0; v < 16; ++v) sacc[rb][v] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
         u32x4_t qf;
         if constexpr (kQRegs) qf = bq[ks];
         else qf = *reinterpret_cast<const u32x4_t*>(sQ + (rb * 32 + l32) * kRS + ks * 16 + half * 8);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
-                                                    __builtin_bit_cast(bf16x8_t, qf), s, 0, 0, 0);
+        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+                                                           __builtin_bit_cast(bf16x8_t, qf), sacc[rb], 0, 0, 0);
       }
+
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      f32x16_t s = sacc[rb];
       // S^T layout: register v holds key 8*(v/4) + 4*half + v%4 of the tile, row l32.
       // Tiles below every row's causal limit and inside the range need no mask.
       float tmax = -INFINITY;

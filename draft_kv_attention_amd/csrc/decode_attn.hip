@@ -315,9 +315,9 @@ __device__ __forceinline__ void issue_tile_lds(u32x4_t* stage, int tile, int k0,
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb0 + o.k + c * CH),
-                                       (lds_ptr_t)(stage + (u * NC + c) * kWave), 16, 0, 0);
+                                       (lds_ptr_t)(stage + (u * NC + c) * kWave), 16, 0, kStreamLoadNT);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb0 + o.v + c * CH),
-                                       (lds_ptr_t)(stage + ((U + u) * NC + c) * kWave), 16, 0, 0);
+                                       (lds_ptr_t)(stage + ((U + u) * NC + c) * kWave), 16, 0, kStreamLoadNT);
     }
   }
 }

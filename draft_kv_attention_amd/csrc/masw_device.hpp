@@ -22,6 +22,12 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;          // LDS-DMA destination
+// Cache policy of the LDS-DMA copies that stream K/V rows read once per launch (the
+// decode kernel, the verifier): the non-temporal hint (`nt`), so the stream does not
+// displace other lines in L2 and the Infinity Cache.  Measured: the 8B verifier layer
+// 103 -> 92-94 us, the fused decode launch about 0.5 us faster.  The prefill re-reads
+// its K/V tiles from L2 across query blocks and keeps the default policy.
+constexpr int kStreamLoadNT = 2;
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;      // LDS transpose-read source
 
 // Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).

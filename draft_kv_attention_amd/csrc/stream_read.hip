@@ -3,7 +3,7 @@
 // attention kernels' achieved GB/s are read; it is not part of the method.
 //
 // Each work-group reads one contiguous chunk of 16-byte words with kUnroll loads in
-// flight per lane, adds the 32-bit words modulo 2^32, reduces across the work-group
+// flight per lane (non-temporal, like the attention kernels' K/V streams), adds the 32-bit words modulo 2^32, reduces across the work-group
 // through LDS and adds its total into sums[blockIdx % MASW_STREAM_SUMS] with one atomic
 // (spread so that the atomics of thousands of work-groups do not queue on one word).
 #include "masw_internal.hpp"
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4_t
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const long j = i + long(kReadThreads) * u;
-      v[u] = j < end ? p[j] : u32x4_t{0, 0, 0, 0};
+      v[u] = j < end ? __builtin_nontemporal_load(&p[j]) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc += v[u].x + v[u].y + v[u].z + v[u].w;

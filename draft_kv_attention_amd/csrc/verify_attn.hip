@@ -287,9 +287,9 @@ __device__ __forceinline__ void verify_issue(u32x4_t* stage, const uint16_t* kba
     const int key = min(tile + row, k1 - 1);   // rows past the range re-read the last key (masked)
     const int chunk = slot ^ tile_swz(row);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + size_t(key) * kD + chunk * 8),
-                                     (lds_ptr_t)(stage + q * kWave), 16, 0, 0);
+                                     (lds_ptr_t)(stage + q * kWave), 16, 0, kStreamLoadNT);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + size_t(key) * kD + chunk * 8),
-                                     (lds_ptr_t)(stage + (kVWaveKeys / 4 + q) * kWave), 16, 0, 0);
+                                     (lds_ptr_t)(stage + (kVWaveKeys / 4 + q) * kWave), 16, 0, kStreamLoadNT);
   }
 }
 

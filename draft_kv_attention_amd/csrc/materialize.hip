@@ -173,9 +173,10 @@ __global__ __launch_bounds__(kPWaves * kWave) void project_mfma_kernel(const Pro
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = kk + 4 * kq + i;
-        wv[p][i] = on && k < a.hidden
-                       ? *reinterpret_cast<const u32x4_t*>(Wm + size_t(k) * N + wcol)
-                       : u32x4_t{0, 0, 0, 0};
+        // At a boundary every weight is read once per launch (non-temporal); a prefill's
+        // row blocks share them through L2 (default policy).
+        const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(Wm + size_t(k) * N + wcol);
+        wv[p][i] = on && k < a.hidden ? (RG == 1 ? __builtin_nontemporal_load(wp) : *wp) : u32x4_t{0, 0, 0, 0};
       }
       const int ka = kk + (lane >> 4) * 8;
 #pragma unroll

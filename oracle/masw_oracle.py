@@ -410,8 +410,9 @@ def append_is_legal(i: int, n_slots: int, S: int, W: int, r: int, rollback: int 
     return n_slots >= m
 
 
-def physical_keylist(t: int, S: int, W: int, r: int) -> List[Tuple[int, int, int]]:
-    """(segment, row, id) per logical key: segment 0 sink (row i-1), 1 ring, 2 slot (row m-1)."""
+def physical_keylist(t: int, S: int, W: int, r: int, rollback: int = 0) -> List[Tuple[int, int, int]]:
+    """(segment, row, id) per logical key: segment 0 sink (row i-1), 1 ring (row
+    (i-S-1) mod (W + r + rollback)), 2 slot (row m-1)."""
     out = []
     for kind, idx in keylist(t, S, W, r):
         if kind == "slot":
@@ -419,7 +420,7 @@ def physical_keylist(t: int, S: int, W: int, r: int) -> List[Tuple[int, int, int
         elif idx <= S:
             out.append((0, idx - 1, idx))
         else:
-            out.append((1, ring_cell(idx, S, W, r), idx))
+            out.append((1, ring_cell(idx, S, W, r, rollback), idx))
     return out
 
 

@@ -39,14 +39,15 @@ def edge_positions(S, W, r):
 # key resolver: bit-exact against the oracle's key list and placement
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("S,W,r", [(4, 32, 16), (0, 5, 2), (3, 4, 4), (2, 6, 1), (7, 8, 5),
-                                   (4, 2048, 64), (128, 128, 4)])
-def test_keylist_bit_exact(S, W, r):
-    ts = [0] + edge_positions(S, W, r) + [S + W + 37 * r + 11]
+@pytest.mark.parametrize("S,W,r,R", [(4, 32, 16, 0), (0, 5, 2, 0), (3, 4, 4, 0), (2, 6, 1, 0), (7, 8, 5, 0),
+                                     (4, 2048, 64, 0), (128, 128, 4, 0), (2, 3, 2, 1), (4, 32, 16, 5),
+                                     (0, 5, 2, 3), (4, 2048, 64, 16), (3, 8, 0, 0)])
+def test_keylist_bit_exact(S, W, r, R):
+    ts = [0] + edge_positions(S, W, max(r, 1)) + [S + W + 37 * max(r, 1) + 11]
     B = len(ts)
     max_slots = O.visible_slot_count(max(ts), S, W, r) + 1
     d = M.Dims(batch=B, n_q_heads=2, n_kv_heads=1, head_dim=64, sink=S, window=W, interval=r,
-               max_slots=max_slots, dtype=torch.float32)
+               max_slots=max_slots, dtype=torch.float32, rollback=R)
     seq = M.alloc_seq(B, DEV)
     seq.seq_len.copy_(torch.tensor(ts, dtype=torch.int32))
     max_keys = S + W + max_slots + 1
@@ -54,7 +55,7 @@ def test_keylist_bit_exact(S, W, r):
         got = M.masw_debug_keylist(d, seq, back=back, max_keys=max_keys).cpu().numpy()
         for b, t in enumerate(ts):
             tv = t - back
-            want = np.array(O.physical_keylist(tv, S, W, r) if tv >= 1 else [], dtype=np.int32).reshape(-1, 3)
+            want = np.array(O.physical_keylist(tv, S, W, r, R) if tv >= 1 else [], dtype=np.int32).reshape(-1, 3)
             n = want.shape[0]
             np.testing.assert_array_equal(got[b, :n], want, err_msg=f"t={t} back={back}")
             assert (got[b, n:] == -1).all()

@@ -112,6 +112,15 @@ def test_window_hand_example():
         assert keys == [("raw", i) for i in c["raw"]] + [("slot", m) for m in c["slots"]]
 
 
+def test_physical_keylist_hand_example():
+    """Placement of every key (sink row, ring row with and without rollback rows, slot
+    row), worked by hand (tests/golden)."""
+    g = _load("physical_keylist_hand_example.json")
+    for c in g["cases"]:
+        got = O.physical_keylist(c["t"], g["S"], g["W"], g["r"], rollback=c["R"])
+        assert [list(k) for k in got] == c["keys"], c
+
+
 def test_no_slot_window_hand_example():
     """Reading R8: without a slot chain the memory is sinks ++ the exact window."""
     g = _load("no_slot_window_hand_example.json")

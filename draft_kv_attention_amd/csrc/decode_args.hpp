@@ -11,61 +11,21 @@
 
 namespace masw {
 
-// Decode streaming.  With MASW_DECODE_LDS_PIPE each wave keeps MASW_DECODE_PIPE_STAGES
-// tiles in flight as asynchronous global->LDS copies (global_load_lds_dwordx4) and
-// reduces the oldest one from registers, so the VALU work of one tile overlaps the
-// memory time of the next ones.  Otherwise tiles are loaded straight into registers,
-// optionally double-buffered.  MASW_DECODE_TILE_KEYS (0: per instantiation, see
-// decode_tile_keys) and MASW_DECODE_NT (non-temporal hint) apply to the register path.
-#ifndef MASW_DECODE_LDS_PIPE
-#define MASW_DECODE_LDS_PIPE 1
-#endif
-#ifndef MASW_DECODE_PIPE_STAGES
-#define MASW_DECODE_PIPE_STAGES 2
-#endif
-#ifndef MASW_DECODE_PIPE_STAGE_INSTR
-#define MASW_DECODE_PIPE_STAGE_INSTR 8
-#endif
-#ifndef MASW_DECODE_TILE_KEYS
-#define MASW_DECODE_TILE_KEYS 0
-#endif
-#ifndef MASW_DECODE_DOUBLE_BUFFER
-#define MASW_DECODE_DOUBLE_BUFFER 0
-#endif
-#ifndef MASW_DECODE_NT
-#define MASW_DECODE_NT 0
-#endif
-#ifndef MASW_DECODE_THREADS
-#define MASW_DECODE_THREADS 256
-#endif
-constexpr bool kDecodeLdsPipe = MASW_DECODE_LDS_PIPE != 0;
-constexpr int kPipeStages = MASW_DECODE_PIPE_STAGES;
-constexpr int kPipeStageInstr = MASW_DECODE_PIPE_STAGE_INSTR;   // 1 KB load instructions per stage
-constexpr bool kDecodeDoubleBuffer = MASW_DECODE_DOUBLE_BUFFER != 0;
-constexpr bool kDecodeNonTemporal = MASW_DECODE_NT != 0;
-constexpr int kDecodeThreads = MASW_DECODE_THREADS;
-static_assert(!kDecodeLdsPipe || (kPipeStages >= 2 && kPipeStages <= 3), "two or three stages");
-static_assert(!kDecodeLdsPipe || kPipeStageInstr * (kPipeStages - 1) <= 63, "s_waitcnt vmcnt holds 6 bits");
-// LDS of the pipeline per work-group (it must leave room for the merge buffers).
-constexpr int kPipeLdsBytes = (kDecodeThreads / 64) * kPipeStages * kPipeStageInstr * 1024;
-static_assert(!kDecodeLdsPipe || kPipeLdsBytes <= 128 * 1024, "pipeline LDS fits beside the merge buffers");
-// Decode work-groups per CU that the split heuristic aims for.  Measured on the 3B layer
-// share (B = 8, 8 KV heads, 2.5K keys): one work-group per CU (4 splits) beats two
-// (8 splits) for every loop variant, the extra partials and merge traffic costing more
-// than the extra waves gain.
+// Decode streaming: each wave keeps kPipeStages tiles in flight as asynchronous
+// global->LDS copies (global_load_lds_dwordx4, kPipeStageInstr 1 KB copies per tile) and
+// reduces the oldest one from registers, so the vector work of one tile overlaps the
+// memory time of the next.  Measured on the 3B layer share (B = 8, t = 32768): three or
+// four stages per wave, eight-wave work-groups and two work-groups per CU were all
+// slower than two stages, four waves and one work-group per CU (see the design notes).
+constexpr int kDecodeThreads = 256;
+constexpr int kPipeStages = 2;
+constexpr int kPipeStageInstr = 8;   // 1 KB load instructions per stage
+// Decode work-groups per CU that the split heuristic aims for.
 constexpr int kDecodeResidentPerCU = 1;
 
-// Keys per wave tile.  Pipeline: one stage holds the K and V rows of a tile,
-// kPipeStageInstr x 64 lanes x 16 bytes.  Register path: as many K/V bytes in flight
-// per wave as fit beside the G query fragments and accumulators without dropping below
-// two waves per SIMD (bf16, D = 128: 64 keys for G <= 3).
-template <int ELEM_BYTES, int D, int G>
-constexpr int decode_tile_keys() {
-  if (kDecodeLdsPipe) return kPipeStageInstr * 1024 / (2 * D * ELEM_BYTES);
-  if (MASW_DECODE_TILE_KEYS > 0) return MASW_DECODE_TILE_KEYS;
-  if (ELEM_BYTES == 2) return G <= 3 || D == 64 ? 64 : 32;
-  return 32;
-}
+// Keys per wave tile: one stage holds the K and V rows of a tile.
+template <int ELEM_BYTES, int D>
+constexpr int decode_tile_keys() { return kPipeStageInstr * 1024 / (2 * D * ELEM_BYTES); }
 
 // Split-K decode attention over one memory (three segments; a full cache is the sink
 // segment alone).  One work-group per (split, KV head, sequence).  With several splits

@@ -10,24 +10,30 @@
 //           key list of one (sequence, KV head); each of its 4 waves streams an equal
 //           contiguous quarter of the chunk in tiles of TK keys (decode_tile_keys), two
 //           tiles in flight as asynchronous global->LDS copies while it reduces the
-//           previous one (register-staged variants remain behind build switches).
+//           previous one.
+//   tiles = the logical key list is a few physical runs (sinks, the ring before and
+//           after its wrap, the slots; new tokens of a fused append come from the
+//           caller's buffer).  A tile inside one run is addressed from a wave-uniform
+//           base plus a per-lane constant; only tiles that straddle runs, hold new
+//           tokens or end the wave's range resolve every row through resolve_key().
 //   wave  = 64/LPR rows of LPR lanes; a row holds one key.  bf16: 8 lanes x 32 bytes
 //           per 256-byte row (D = 128), so a load instruction pair moves 8 whole rows;
 //           q.k partial dots use v_dot2_f32_bf16 and are summed over the 8 lanes with
-//           three DPP steps.  P.V also runs on v_dot2_f32_bf16: a lane pairs two of its
+//           three DPP adds.  P.V also runs on v_dot2_f32_bf16: a lane pairs two of its
 //           rows (one v_perm_b32 per dword) and P is rounded to bf16 for that product,
 //           the usual flash-attention precision; the running sum l stays fp32.
 //           fp32 (small models): 16 lanes per row and plain FMAs.
-//   softmax is online (running max in log2 units, rescale per tile); each wave sums
-//   its row groups as a reduce-scatter and the waves merge through LDS; splits merge
-//   in the same launch: every work-group writes an (max, sum, o) partial and the last
-//   one to finish its (sequence, KV head) - found with an atomic ticket, reset to zero
-//   afterwards - merges them (flash-decoding without a second kernel).
-// Every key row is located through resolve_key(), which maps the logical index to
-// sink row i-1, ring row (i-S-1) mod (W+r) or slot row m-1 on the device, so no host
-// round trip is needed when t changes.  With a fused append the newest n_new raw
-// tokens are read straight from the caller's k_new/v_new and split 0 writes them into
-// the memory (rows no other work-group of this launch reads).
+//   softmax is online (running max in log2 units, rescale when it grows); each wave
+//   sums its row groups as a reduce-scatter and the waves merge through LDS.
+//   splits merge in the same launch: every work-group stores an (max, sum, o) partial
+//   and takes a ticket; the last one to arrive for its (sequence, KV head) - found with
+//   an atomic ticket, reset to zero afterwards - loads the others in one round trip and
+//   merges them (flash-decoding without a second kernel).
+// Row addresses agree with resolve_key(), which maps the logical index to sink row
+// i-1, ring row (i-S-1) mod (W+r) or slot row m-1 on the device, so no host round
+// trip is needed when t changes.  With a fused append the newest n_new raw tokens are
+// read straight from the caller's k_new/v_new and split 0 writes them into the memory
+// (rows no other work-group of this launch reads).
 #include "decode_args.hpp"
 
 namespace masw {
@@ -59,30 +65,17 @@ __device__ __forceinline__ int decode_keys(const DecodeArgs& a, int t, int have,
   return ks.total();
 }
 
+constexpr int kWaves = kDecodeThreads / kWave;
+
 // Keys per split: ceil(n / splits) rounded up to a multiple of kSplitRound, so that
 // the waves of a work-group each take an equal contiguous run of whole 8-row groups.
 // A function of (n, splits) only, so two memories with the same key list reduce in
 // the same order.
-constexpr int kSplitRound = 8 * (kDecodeThreads / kWave);
+constexpr int kSplitRound = 8 * kWaves;
 __device__ __forceinline__ int split_chunk(int n, int n_splits) {
   int c = (n + n_splits - 1) / n_splits;
   return (c + kSplitRound - 1) / kSplitRound * kSplitRound;
 }
-
-// A lane fragment of one row: NW dwords in 16-byte chunks; chunk c sits CH elements
-// after chunk 0, so the LPR lanes of a row together cover each 128/256-byte span of the
-// row contiguously (one load instruction reads whole cache lines).
-template <int NW, int CH, typename T>
-__device__ __forceinline__ void load_frag(uint32_t (&w)[NW], const T* p) {
-  static_assert(NW % 4 == 0, "fragments are whole 16-byte chunks");
-#pragma unroll
-  for (int c = 0; c < NW / 4; ++c) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p + c * CH);
-    const u32x4_t x = kDecodeNonTemporal ? __builtin_nontemporal_load(src) : *src;
-    w[4 * c] = x.x; w[4 * c + 1] = x.y; w[4 * c + 2] = x.z; w[4 * c + 3] = x.w;
-  }
-}
-
 
 template <typename T, int NW>
 __device__ __forceinline__ float frag_dot(const uint32_t (&a)[NW], const uint32_t (&b)[NW]) {
@@ -165,8 +158,6 @@ __device__ void append_rows(const DecodeArgs& a, int b, int kvh, int t, int have
   if (bits && report) atomicOr(a.err, bits);
 }
 
-constexpr int kMergeBatch = 8;    // split partials one thread loads at once
-
 // Two adjacent outputs (d even) in one store.
 template <typename T>
 __device__ __forceinline__ void store_out2(T* p, float v0, float v1) {
@@ -176,61 +167,80 @@ __device__ __forceinline__ void store_out2(T* p, float v0, float v1) {
     *reinterpret_cast<float2*>(p) = make_float2(v0, v1);
 }
 
-// Combine n_valid (max, sum, o) partials of the G query heads of one KV head into out.
-// No LDS and no barrier: every thread takes two adjacent outputs (g, d), (g, d + 1) and
-// loads, for a batch of splits, their o pairs and (max, sum) pairs as 8-byte words
-// straight into registers (every load of the batch, for all of the thread's outputs, in
-// flight together), then folds the batch in online, rescaling what it has when the
-// running max grows.  One round trip when n_valid <= kMergeBatch.
-template <typename T, int D, int G>
-__device__ __forceinline__ void merge_partials(const float* part_o, const float* part_ml, size_t row0, int n_splits,
-                                               int n_valid, T* outb) {
-  constexpr int NP = G * D / 2;                                     // output pairs
-  constexpr int PER = (NP + kDecodeThreads - 1) / kDecodeThreads;   // pairs per thread
-  float M[PER], L[PER], O0[PER], O1[PER];
+// ---------------------------------------------------------------------------
+// Split merge
+// ---------------------------------------------------------------------------
+// Every work-group of a (sequence, KV head) stores its (max, sum, o) partial, waits for
+// the stores and takes a ticket (split_arrive); the last arrival folds all partials.
+// Each merging thread loads the partials of up to merge_batch<PER>() splits at once -
+// every split of the batch-1 and batch-8 plans - so the merge costs one memory round
+// trip; its own partial it takes from registers.
+template <int PER>
+constexpr int merge_batch() { return PER == 1 ? 32 : (PER == 2 ? 16 : 8); }
+
+struct Partial {
+  float m, l, o0, o1;
+};
+
+// Fold partials into the running (M, L, O0, O1) of one output pair, online: the batch
+// max first, then every partial weighted against it (absent splits carry -inf).
+template <int N>
+__device__ __forceinline__ void fold_partials(const Partial (&p)[N], float& M, float& L, float& O0, float& O1) {
+  float mb = M;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) { M[k] = -INFINITY; L[k] = 0.f; O0[k] = 0.f; O1[k] = 0.f; }
-  for (int s0 = 0; s0 < n_valid; s0 += kMergeBatch) {
-    float2 ml[PER][kMergeBatch], v[PER][kMergeBatch];
+  for (int j = 0; j < N; ++j) mb = fmaxf(mb, p[j].m);
+  const float alpha = fast_exp2(M - mb);   // 0 on the first batch (M = -inf)
+  L *= alpha;
+  O0 *= alpha;
+  O1 *= alpha;
+  M = mb;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int pi = threadIdx.x + k * kDecodeThreads;
-      const int g = 2 * pi / D, d = 2 * pi - g * D;
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const bool ok = (PER * kDecodeThreads == NP || pi < NP) && s0 + j < n_valid;
-        ml[k][j] = ok ? load_partial2(part_ml + ((row0 + g) * n_splits + s0 + j) * 2) : make_float2(-INFINITY, 0.f);
-        v[k][j] = ok ? load_partial2(part_o + ((row0 + g) * n_splits + s0 + j) * D + d) : make_float2(0.f, 0.f);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      float mb = M[k];
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, ml[k][j].x);
-      const float alpha = fast_exp2(M[k] - mb);   // 0 on the first batch (M = -inf)
-      L[k] *= alpha;
-      O0[k] *= alpha;
-      O1[k] *= alpha;
-      M[k] = mb;
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const float wt = fast_exp2(ml[k][j].x - mb);   // splits past n_valid carry -inf -> 0
-        L[k] = fmaf(wt, ml[k][j].y, L[k]);
-        O0[k] = fmaf(wt, v[k][j].x, O0[k]);
-        O1[k] = fmaf(wt, v[k][j].y, O1[k]);
-      }
-    }
+  for (int j = 0; j < N; ++j) {
+    const float wt = fast_exp2(p[j].m - mb);
+    L = fmaf(wt, p[j].l, L);
+    O0 = fmaf(wt, p[j].o0, O0);
+    O1 = fmaf(wt, p[j].o1, O1);
   }
+}
+
+// Fold the n_valid partials of the G query heads of one KV head, in split order, into
+// `out` (PER output pairs per thread).  The fold order does not depend on which
+// work-group merges, so the result is the same bits whichever one arrives last.
+template <typename T, int D, int G, int PER>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, size_t row0, int n_valid, int own,
+                                               const Partial (&mine)[PER], T* outb) {
+  constexpr int NP = G * D / 2;
+  constexpr int NB = merge_batch<PER>();
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int pi = threadIdx.x + k * kDecodeThreads;
     if (PER * kDecodeThreads != NP && pi >= NP) break;
     const int g = 2 * pi / D, d = 2 * pi - g * D;
-    store_out2<T>(outb + g * D + d, O0[k] / L[k], O1[k] / L[k]);
+    const float* pml = a.part_ml + (row0 + g) * a.n_splits * 2;
+    const float* po = a.part_o + (row0 + g) * a.n_splits * D + d;
+    float M = -INFINITY, L = 0.f, O0 = 0.f, O1 = 0.f;
+    for (int s0 = 0; s0 < n_valid; s0 += NB) {
+      float2 ml[NB], v[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int s = s0 + j;
+        const bool ld = s < n_valid && s != own;
+        ml[j] = ld ? load_partial2(pml + 2 * s) : make_float2(-INFINITY, 0.f);
+        v[j] = ld ? load_partial2(po + size_t(s) * D) : make_float2(0.f, 0.f);
+      }
+      Partial p[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        p[j] = s0 + j == own ? mine[k] : Partial{ml[j].x, ml[j].y, v[j].x, v[j].y};
+      fold_partials(p, M, L, O0, O1);
+    }
+    store_out2<T>(outb + g * D + d, O0 / L, O1 / L);
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row layout and reductions
+// ---------------------------------------------------------------------------
 // Lanes per key row: bf16 uses 8 lanes x 32 bytes (3 DPP steps per row reduction),
 // fp32 16 lanes.  A wave instruction then covers 64 / LPR rows.
 template <typename T> struct RowLayout { static constexpr int LPR = sizeof(T) == 2 ? 8 : 16; };
@@ -241,10 +251,7 @@ __device__ __forceinline__ float row_sum(float v) {
     return row16_sum(v);
   } else {
     // quad xor 1, quad xor 2, then mirror inside the 8-lane half row
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false));
-    return v;
+    return dpp_add<0x141>(dpp_add<0x4E>(dpp_add<0xB1>(v)));
   }
 }
 
@@ -256,10 +263,13 @@ __device__ __forceinline__ float groups_max(float v) {
 }
 template <int LPR>
 __device__ __forceinline__ float groups_sum(float v) {
-  if constexpr (LPR == 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+  if constexpr (LPR == 8) v = dpp_add<0x128>(v);
   return rows4_sum(v);
 }
 
+// ---------------------------------------------------------------------------
+// Tile addressing
+// ---------------------------------------------------------------------------
 // Where a lane's rows live, as element offsets from the sink base of K (and of V): the
 // ring, slot and new-token blocks are separate allocations, so each is one 64-bit
 // delta.  Keeping them as plain values (no struct or array of pointers to index) lets
@@ -284,34 +294,84 @@ __device__ __forceinline__ RowOff row_offsets(int j, const KeySpan& ks, const Me
   return RowOff{dk + row, dv + row};
 }
 
-// Issue the loads of one tile: row u of this lane is logical key tile + u*RPI + lgrp
-// (rows past k1 re-read row k0 and are masked in the reduction).
-template <typename T, int D, int U, int NW, int CH, int RPI>
-__device__ __forceinline__ void load_tile(uint32_t (&fk)[U][NW], uint32_t (&fv)[U][NW], int tile, int k0, int k1,
-                                          int lgrp, const KeySpan& ks, const MemGeom& g, const T* kb0,
-                                          const T* vb0, const TileSrc src) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = tile + u * RPI + lgrp;
-    const RowOff o = row_offsets<D>(j < k1 ? j : k0, ks, g, src);
-    load_frag<NW, CH>(fk[u], kb0 + o.k);
-    load_frag<NW, CH>(fv[u], vb0 + o.v);
-  }
+// The runs of the logical key list that are contiguous rows of one memory block:
+// keys [lo, hi) of run r sit at element offset off_k + j * D from the K sink base (V
+// alike).  Run 0: sinks already in memory; 1, 2: window rows in the ring before and
+// after its wrap; 3: slots.  New tokens of a fused append are in none of them.
+struct KeyRuns {
+  int lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
+  long k0, v0, k1, v1, k2, v2, k3, v3;
+};
+
+template <int D>
+__device__ __forceinline__ KeyRuns key_runs(const KeySpan& ks, const MemGeom& g, const TileSrc& src) {
+  KeyRuns r;
+  r.lo0 = 0;
+  r.hi0 = min(ks.ns, src.t_old);                                      // sink ids j + 1 <= t_old
+  r.k0 = 0;
+  r.v0 = 0;
+  const int n_old = max(0, min(ks.nl, src.t_old - ks.lo + 1));        // window rows in the ring
+  const int to_wrap = g.C - ks.ring0;
+  r.lo1 = ks.ns;
+  r.hi1 = ks.ns + min(n_old, to_wrap);
+  r.k1 = src.dk_ring + long(ks.ring0 - ks.ns) * D;
+  r.v1 = src.dv_ring + long(ks.ring0 - ks.ns) * D;
+  r.lo2 = ks.ns + to_wrap;
+  r.hi2 = ks.ns + n_old;                                              // empty unless it wraps
+  r.k2 = src.dk_ring - long(ks.ns + to_wrap) * D;
+  r.v2 = src.dv_ring - long(ks.ns + to_wrap) * D;
+  r.lo3 = ks.ns + ks.nl;
+  r.hi3 = ks.total();
+  r.k3 = src.dk_slot - long(ks.ns + ks.nl) * D;
+  r.v3 = src.dv_slot - long(ks.ns + ks.nl) * D;
+  return r;
 }
 
-// The same tile as asynchronous copies into one LDS stage of this wave: load
-// instruction i (K rows, then V rows; chunk-major inside a row) writes 64 lanes x 16
-// bytes at stage + i KB, lane l at byte 16 l, so read_tile_lds hands every lane exactly
-// the fragment load_tile would have loaded.  Completion is tracked by vmcnt only.
-template <typename T, int D, int U, int NW, int CH, int RPI>
-__device__ __forceinline__ void issue_tile_lds(u32x4_t* stage, int tile, int k0, int k1, int lgrp,
-                                               const KeySpan& ks, const MemGeom& g, const T* kb0, const T* vb0,
-                                               const TileSrc src) {
+// Issue the copies of one tile into one LDS stage of this wave: load instruction i (K
+// rows, then V rows; chunk-major inside a row) writes 64 lanes x 16 bytes at stage + i
+// KB, lane l at byte 16 l, so every lane later reads back exactly its own fragments.
+// Row u of this lane is logical key tile + u*RPI + lgrp.  A tile inside one run (all
+// values wave-uniform) takes its row addresses from one base plus a per-lane constant;
+// any other tile resolves each row (rows past w1 re-read row w0 and are masked in the
+// reduction).  Completion is tracked by vmcnt only.
+template <typename T, int D, int U, int NW, int CH, int RPI, int TK>
+__device__ __forceinline__ void issue_tile(u32x4_t* stage, int tile, int w0, int w1, int lgrp, const KeySpan& ks,
+                                           const MemGeom& g, const T* kb0, const T* vb0, const TileSrc& src,
+                                           const KeyRuns& runs) {
   constexpr int NC = NW / 4;
+  bool fast = false;
+  long bk = 0, bv = 0;
+  if (tile + TK <= w1) {
+    if (tile + TK <= runs.hi0) {
+      fast = true; bk = runs.k0; bv = runs.v0;
+    } else if (tile >= runs.lo1 && tile + TK <= runs.hi1) {
+      fast = true; bk = runs.k1; bv = runs.v1;
+    } else if (tile >= runs.lo2 && tile + TK <= runs.hi2) {
+      fast = true; bk = runs.k2; bv = runs.v2;
+    } else if (tile >= runs.lo3 && tile + TK <= runs.hi3) {
+      fast = true; bk = runs.k3; bv = runs.v3;
+    }
+  }
+  if (fast) {
+    const T* kt = kb0 + bk + long(tile) * D;
+    const T* vt = vb0 + bv + long(tile) * D;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ro = (u * RPI + lgrp) * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(kt + ro + c * CH),
+                                         (lds_ptr_t)(stage + (u * NC + c) * kWave), 16, 0, kStreamLoadNT);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(vt + ro + c * CH),
+                                         (lds_ptr_t)(stage + ((U + u) * NC + c) * kWave), 16, 0, kStreamLoadNT);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = tile + u * RPI + lgrp;
-    const RowOff o = row_offsets<D>(j < k1 ? j : k0, ks, g, src);
+    const RowOff o = row_offsets<D>(j < w1 ? j : w0, ks, g, src);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb0 + o.k + c * CH),
@@ -322,21 +382,42 @@ __device__ __forceinline__ void issue_tile_lds(u32x4_t* stage, int tile, int k0,
   }
 }
 
+// Read this lane's fragments of a tile back from its LDS stage (load instruction i of
+// the copies wrote 16 bytes per lane at stage + i KB), then wait for the reads
+// (lgkmcnt 0).  The reads are one asm statement: the copies fill the stage behind the
+// compiler's back, the caller has waited for them (vmcnt), and the compiler must
+// neither move the reads nor add waits of its own for the copies in flight.
 template <int U, int NW>
 __device__ __forceinline__ void read_tile_lds(uint32_t (&fk)[U][NW], uint32_t (&fv)[U][NW], const u32x4_t* stage,
                                               int lane) {
   constexpr int NC = NW / 4;
+  static_assert(2 * U * NC == 8, "a stage is eight 1 KB copies: K rows, then V rows");
+  const uint32_t addr = uint32_t(reinterpret_cast<uintptr_t>(stage + lane));
+  u32x4_t x0, x1, x2, x3, x4, x5, x6, x7;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4), "=&v"(x5), "=&v"(x6), "=&v"(x7)
+      : "v"(addr)
+      : "memory");
+  const u32x4_t x[8] = {x0, x1, x2, x3, x4, x5, x6, x7};
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u32x4_t x = stage[(u * NC + c) * kWave + lane];
-      const u32x4_t y = stage[((U + u) * NC + c) * kWave + lane];
-      fk[u][4 * c] = x.x; fk[u][4 * c + 1] = x.y; fk[u][4 * c + 2] = x.z; fk[u][4 * c + 3] = x.w;
-      fv[u][4 * c] = y.x; fv[u][4 * c + 1] = y.y; fv[u][4 * c + 2] = y.z; fv[u][4 * c + 3] = y.w;
-    }
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fk[u][4 * c + i] = x[u * NC + c][i];
+        fv[u][4 * c + i] = x[(U + u) * NC + c][i];
+      }
 }
-
 
 // Online-softmax update of (m, l, acc) with one tile.
 template <typename T, int G, int U, int NW, int EPL, int LPR, int RPI>
@@ -447,11 +528,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   constexpr int NW = EPL * int(sizeof(T)) / 4;   // dwords per lane of one row
   constexpr int VEC = 16 / int(sizeof(T));       // elements per 16-byte chunk
   constexpr int CH = LPR * VEC;                  // elements between a lane's chunks
-  constexpr int TK = decode_tile_keys<int(sizeof(T)), D, G>();   // keys per wave tile
+  constexpr int TK = decode_tile_keys<int(sizeof(T)), D>();   // keys per wave tile
   constexpr int U = TK / RPI;                    // rows per lane per tile
-  constexpr int NWAVES = kDecodeThreads / kWave;
+  constexpr int KI = 2 * U * (NW / 4);           // load instructions per tile
+  constexpr int NP = G * D / 2;                  // output pairs of one KV head
+  constexpr int PER = (NP + kDecodeThreads - 1) / kDecodeThreads;   // pairs per thread
   static_assert(U % 2 == 0, "rows are paired for the bf16 P.V dot products");
-  static_assert(kSplitRound % (NWAVES * RPI) == 0, "a wave's run is whole row groups");
+  static_assert(kSplitRound % (kWaves * RPI) == 0, "a wave's run is whole row groups");
+  static_assert(KI == kPipeStageInstr, "a stage holds exactly one tile");
+  static_assert(kPipeStages == 2, "the wait below assumes two stages");
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (kWave - 1);
@@ -460,13 +545,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   const int lsub = lane % LPR;
 
   // Start-up loads are independent of each other: issue them together.
+  // (Absent per-sequence arrays read seq_len instead, so the three scalar loads go out
+  // together without branches.)
   const int t = a.seq_len[b];
-  const int have = a.n_slots ? a.n_slots[b] : 0;
-  const int act = a.active ? a.active[b] : 1;
+  const int have_raw = (a.n_slots ? a.n_slots : a.seq_len)[b];
+  const int act_raw = (a.active ? a.active : a.seq_len)[b];
+  const int have = a.n_slots ? have_raw : 0;
+  const int act = a.active ? act_raw : 1;
   uint32_t qw[G][NW];
   const T* qb = static_cast<const T*>(a.q) + size_t(b) * a.qo_stride + size_t(kvh) * G * D + lsub * VEC;
 #pragma unroll
-  for (int g = 0; g < G; ++g) load_frag<NW, CH>(qw[g], qb + g * D);
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int c = 0; c < NW / 4; ++c) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qb + g * D + c * CH);
+      qw[g][4 * c] = x.x; qw[g][4 * c + 1] = x.y; qw[g][4 * c + 2] = x.z; qw[g][4 * c + 3] = x.w;
+    }
 
   // Split 0 of every (sequence, KV head) also appends the new tokens: loads now, stores
   // after its share of the keys.
@@ -484,23 +578,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     if (appender) append_rows<T, D>(a, b, kvh, t, have, kvh == 0, apk, apv);
     return;
   }
-  const int chunk = split_chunk(n, a.n_splits);
+  const int chunk = __builtin_amdgcn_readfirstlane(split_chunk(n, a.n_splits));
   const int k0 = split * chunk;
   if (k0 >= n) return;
-  const int k1 = min(k0 + chunk, n);
+  const int k1 = __builtin_amdgcn_readfirstlane(min(k0 + chunk, n));
   const int n_valid = (n + chunk - 1) / chunk;
 
+  // Block bases of this (sequence, KV head): wave-uniform, so every offset between them
+  // stays in scalar registers; each lane adds its own column offset lsub * VEC.
   const size_t unit = size_t(b) * a.Hkv + kvh;
-  const T* kb0 = static_cast<const T*>(a.k[0]) + unit * a.cap[0] * D + lsub * VEC;
-  const T* kb1 = static_cast<const T*>(a.k[1]) + unit * a.cap[1] * D + lsub * VEC;
-  const T* kb2 = static_cast<const T*>(a.k[2]) + unit * a.cap[2] * D + lsub * VEC;
-  const T* vb0 = static_cast<const T*>(a.v[0]) + unit * a.cap[0] * D + lsub * VEC;
-  const T* vb1 = static_cast<const T*>(a.v[1]) + unit * a.cap[1] * D + lsub * VEC;
-  const T* vb2 = static_cast<const T*>(a.v[2]) + unit * a.cap[2] * D + lsub * VEC;
+  const T* ku0 = static_cast<const T*>(a.k[0]) + unit * a.cap[0] * D;
+  const T* ku1 = static_cast<const T*>(a.k[1]) + unit * a.cap[1] * D;
+  const T* ku2 = static_cast<const T*>(a.k[2]) + unit * a.cap[2] * D;
+  const T* vu0 = static_cast<const T*>(a.v[0]) + unit * a.cap[0] * D;
+  const T* vu1 = static_cast<const T*>(a.v[1]) + unit * a.cap[1] * D;
+  const T* vu2 = static_cast<const T*>(a.v[2]) + unit * a.cap[2] * D;
   const int t_old = t - a.n_new;   // positions above this come from k_new / v_new
   const size_t new_row = size_t(a.Hkv) * D;
-  const T* knb = a.n_new ? static_cast<const T*>(a.k_new) + (size_t(b) * a.n_new * a.Hkv + kvh) * D + lsub * VEC : kb0;
-  const T* vnb = a.n_new ? static_cast<const T*>(a.v_new) + (size_t(b) * a.n_new * a.Hkv + kvh) * D + lsub * VEC : vb0;
+  const T* knu = a.n_new ? static_cast<const T*>(a.k_new) + (size_t(b) * a.n_new * a.Hkv + kvh) * D : ku0;
+  const T* vnu = a.n_new ? static_cast<const T*>(a.v_new) + (size_t(b) * a.n_new * a.Hkv + kvh) * D : vu0;
+  const T* kb0 = ku0 + lsub * VEC;
+  const T* vb0 = vu0 + lsub * VEC;
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -511,67 +609,46 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  const TileSrc src{long(kb1 - kb0), long(kb2 - kb0), long(knb - kb0), long(vb1 - vb0), long(vb2 - vb0),
-                     long(vnb - vb0), long(new_row), t_old};
+  const TileSrc src{long(ku1 - ku0), long(ku2 - ku0), long(knu - ku0), long(vu1 - vu0), long(vu2 - vu0),
+                    long(vnu - vu0), long(new_row), t_old};
+  const KeyRuns runs = key_runs<D>(ks, a.g, src);
   // LDS: the tile stages of the pipeline; once a wave has left its loop its own stages
   // hold its (g, d) accumulators for the merge of the waves.
-  constexpr int KI = 2 * U * (NW / 4);   // load instructions per tile
-  constexpr int WAVE_O = kDecodeLdsPipe ? kPipeStages * KI * kWave * 4 : G * D;   // floats per wave
-  static_assert(!kDecodeLdsPipe || G * D <= WAVE_O, "a wave's stages hold its accumulators");
-  __shared__ u32x4_t pipe[kDecodeLdsPipe ? NWAVES : 1][kDecodeLdsPipe ? kPipeStages : 1][kDecodeLdsPipe ? KI * kWave : 1];
-  __shared__ float sm_o_regs[kDecodeLdsPipe ? 1 : NWAVES * G * D];
-  float* const sm_o = kDecodeLdsPipe ? reinterpret_cast<float*>(&pipe[0][0][0]) : sm_o_regs;
+  constexpr int WAVE_O = kPipeStages * KI * kWave * 4;   // floats per wave
+  static_assert(G * D <= WAVE_O, "a wave's stages hold its accumulators");
+  __shared__ u32x4_t pipe[kWaves][kPipeStages][KI * kWave];
+  float* const sm_o = reinterpret_cast<float*>(&pipe[0][0][0]);
 
   // Wave w streams keys [w0, w1) of the chunk, one tile at a time (the last one ragged).
-  const int sub = chunk / NWAVES;
-  const int w0 = k0 + wave * sub;
-  const int w1 = min(w0 + sub, k1);
-  if constexpr (kDecodeLdsPipe) {
-    // kPipeStages tiles of this wave in flight as global->LDS copies; tile i sits in
-    // stage i mod kPipeStages.  Before tile i is read, s_waitcnt leaves only the copies
-    // of the tiles issued after it outstanding (copies complete in issue order); once
-    // its fragments are in registers (lgkmcnt 0) the stage is refilled with tile
-    // i + kPipeStages and tile i is reduced while the copies stream.
-    static_assert(KI == kPipeStageInstr, "a stage holds exactly one tile");
+  // Tile i sits in stage i mod 2.  Before tile i is read, s_waitcnt leaves only the
+  // copies of tile i + 1 outstanding (copies complete in issue order); once its
+  // fragments are in registers (lgkmcnt 0) the stage is refilled with tile i + 2 and
+  // tile i is reduced while the copies stream.
+  const int sub = chunk / kWaves;
+  const int w0 = __builtin_amdgcn_readfirstlane(k0 + wave * sub);
+  const int w1 = __builtin_amdgcn_readfirstlane(min(w0 + sub, k1));
+  {
     const int nt = w0 < w1 ? (w1 - w0 + TK - 1) / TK : 0;   // tiles of this wave
+    // The query fragments (and the append's prefetched rows) were requested together
+    // with seq_len, whose value every address below needs: wait for them here, once.
+    // Without this explicit wait the compiler cannot tell inside the loop that they have
+    // arrived and waits for every copy in flight (vmcnt 0) before each tile's arithmetic.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 #pragma unroll
     for (int i = 0; i < kPipeStages; ++i)
-      if (i < nt) issue_tile_lds<T, D, U, NW, CH, RPI>(pipe[wave][i], w0 + i * TK, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
+      if (i < nt) issue_tile<T, D, U, NW, CH, RPI, TK>(pipe[wave][i], w0 + i * TK, w0, w1, lgrp, ks, a.g, kb0, vb0, src, runs);
     uint32_t ka[U][NW], va[U][NW];
     int st = 0;
     for (int i = 0; i < nt; ++i) {
-      const int ahead = min(nt - 1 - i, kPipeStages - 1);   // tiles issued after tile i
-      if (kPipeStages == 3 && ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * KI));
-      else if (ahead >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(KI));
+      if (i + 1 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(KI));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       read_tile_lds<U, NW>(ka, va, pipe[wave][st], lane);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       const int tile = w0 + i * TK;
       if (i + kPipeStages < nt)
-        issue_tile_lds<T, D, U, NW, CH, RPI>(pipe[wave][st], tile + kPipeStages * TK, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
+        issue_tile<T, D, U, NW, CH, RPI, TK>(pipe[wave][st], tile + kPipeStages * TK, w0, w1, lgrp, ks, a.g, kb0, vb0, src,
+                                             runs);
       reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, w1, lgrp, a.scale_log2, qw, m, l, acc);
-      st = st + 1 == kPipeStages ? 0 : st + 1;
-    }
-  } else if constexpr (kDecodeDoubleBuffer) {
-    uint32_t ka[U][NW], va[U][NW], kc[U][NW], vc[U][NW];
-    int tile = w0;
-    if (tile < w1) load_tile<T, D, U, NW, CH, RPI>(ka, va, tile, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
-    while (tile < w1) {
-      int nt = tile + TK;
-      if (nt < w1) load_tile<T, D, U, NW, CH, RPI>(kc, vc, nt, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
-      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, w1, lgrp, a.scale_log2, qw, m, l, acc);
-      tile = nt;
-      if (tile >= w1) break;
-      nt = tile + TK;
-      if (nt < w1) load_tile<T, D, U, NW, CH, RPI>(ka, va, nt, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
-      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(kc, vc, tile, w1, lgrp, a.scale_log2, qw, m, l, acc);
-      tile = nt;
-    }
-  } else {
-    uint32_t ka[U][NW], va[U][NW];
-    for (int tile = w0; tile < w1; tile += TK) {
-      load_tile<T, D, U, NW, CH, RPI>(ka, va, tile, w0, w1, lgrp, ks, a.g, kb0, vb0, src);
-      reduce_tile<T, G, U, NW, EPL, LPR, RPI>(ka, va, tile, w1, lgrp, a.scale_log2, qw, m, l, acc);
+      st ^= 1;
     }
   }
 
@@ -583,7 +660,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   groups_reduce_scatter<LPR, G, EPL>(acc, lane);
   constexpr int NF = G * EPL / (kWave / LPR);   // accumulators a lane keeps
 
-  __shared__ float sm_m[NWAVES][G], sm_l[NWAVES][G];
+  __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
   __shared__ int sm_last;
   if (lane == 0) {
 #pragma unroll
@@ -596,24 +673,32 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   }
   __syncthreads();
 
+  const bool merged = n_valid > 1;
   T* outb = static_cast<T*>(a.out) + size_t(b) * a.qo_stride + size_t(kvh) * G * D;
   const size_t row0 = size_t(b) * a.Hq + size_t(kvh) * G;   // partial rows of this KV head
-  // Each thread combines the waves for two adjacent outputs (d, d + 1).
-  for (int pi = threadIdx.x; pi < G * D / 2; pi += kDecodeThreads) {
+  // Each thread combines the waves for PER pairs of adjacent outputs (d, d + 1) and, with
+  // several splits, publishes that partial.
+  Partial mine[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int pi = threadIdx.x + k * kDecodeThreads;
+    mine[k] = Partial{-INFINITY, 0.f, 0.f, 0.f};
+    if (PER * kDecodeThreads != NP && pi >= NP) break;
     const int g = 2 * pi / D, d = 2 * pi - g * D;
     float M = sm_m[0][g];
 #pragma unroll
-    for (int w = 1; w < NWAVES; ++w) M = fmaxf(M, sm_m[w][g]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
     float L = 0.f, O0 = 0.f, O1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWAVES; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float wt = fast_exp2(sm_m[w][g] - M);   // idle waves carry m = -inf -> 0
       const float2 o = *reinterpret_cast<const float2*>(&sm_o[w * WAVE_O + g * D + d]);
       L = fmaf(wt, sm_l[w][g], L);
       O0 = fmaf(wt, o.x, O0);
       O1 = fmaf(wt, o.y, O1);
     }
-    if (n_valid == 1) {
+    mine[k] = Partial{M, L, O0, O1};
+    if (!merged) {
       store_out2<T>(outb + g * D + d, O0 / L, O1 / L);
     } else {
       const size_t pr = (row0 + g) * a.n_splits + split;
@@ -621,51 +706,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       if (d == 0) store_partial2(&a.part_ml[pr * 2], M, L);
     }
   }
-  if (n_valid == 1) {
+  if (!merged) {
     if (a.n_slots_out && kvh == 0 && threadIdx.x == 0) a.n_slots_out[b] = act;
     return;
   }
-#if MASW_SPLIT_MERGE != 0
-  // Split merge: the last work-group of this (sequence, KV head) combines all partials.
-  // Every partial load is issued before any is used: (max, sum) pairs land in LDS,
-  // the o values of up to kMergeBatch splits per thread are in flight together.
+  // The last work-group of this (sequence, KV head) to arrive merges every split's
+  // partial and leaves the ticket at zero for the next call.
   if (!split_arrive(&a.counters[unit], n_valid, &sm_last)) return;
-  merge_partials<T, D, G>(a.part_o, a.part_ml, row0, a.n_splits, n_valid, outb);
+  merge_partials<T, D, G, PER>(a, row0, n_valid, split, mine, outb);
   if (threadIdx.x == 0) {
     reset_ticket(&a.counters[unit]);
     if (a.n_slots_out && kvh == 0) a.n_slots_out[b] = act;
   }
-#else
-  (void)sm_last;
-#endif
-}
-
-// Separate merge pass (MASW_SPLIT_MERGE 0): one work-group per (query head, sequence).
-template <typename T, int D>
-__global__ __launch_bounds__(D) void combine_kernel(const DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int t = a.seq_len[b];
-  const int have = a.n_slots ? a.n_slots[b] : 0;
-  const int act = a.active ? a.active[b] : 1;
-  KeySpan ks;
-  const int n = decode_keys(a, t, have, act, ks, false);
-  if (n == 0) return;
-  const int chunk = split_chunk(n, a.n_splits);
-  const int nv = (n + chunk - 1) / chunk;
-  if (nv == 1) return;   // written directly by the single work-group
-  const size_t row = size_t(b) * a.Hq + h;
-  const float* ml = a.part_ml + row * a.n_splits * 2;
-  const float* po = a.part_o + row * a.n_splits * D + d;
-  float M = -INFINITY;
-  for (int s = 0; s < nv; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < nv; ++s) {
-    const float wt = fast_exp2(ml[2 * s] - M);
-    L = fmaf(wt, ml[2 * s + 1], L);
-    O = fmaf(wt, po[size_t(s) * D], O);
-  }
-  static_cast<T*>(a.out)[size_t(b) * a.qo_stride + size_t(h) * D + d] = Elem<T>::from_f32(O / L);
-  if (a.n_slots_out && h == 0 && d == 0) a.n_slots_out[b] = act;
 }
 
 __global__ void keylist_kernel(const MemGeom g, const int32_t* seq_len, int back, int32_t* out,
@@ -692,9 +744,6 @@ __global__ void keylist_kernel(const MemGeom g, const int32_t* seq_len, int back
 template <typename T, int D, int G>
 int launch_typed(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(a.n_splits, a.Hkv, a.B), dim3(kDecodeThreads), 0, s, a);
-#if MASW_SPLIT_MERGE == 0
-  if (a.n_splits > 1) hipLaunchKernelGGL((combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(D), 0, s, a);
-#endif
   return hipGetLastError() == hipSuccess ? MASW_OK : MASW_ERR_LAUNCH;
 }
 

@@ -70,13 +70,16 @@ template <> struct Elem<uint16_t> {
 // ---------------------------------------------------------------------------
 // Cross-lane reductions
 // ---------------------------------------------------------------------------
+// v + (v of the lane a DPP control selects).  The identity as the "old" operand lets the
+// compiler fold the move into the add (v_add_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
 // Sum over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1): every lane gets the total.
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, false));
-  return v;
+  return dpp_add<0x121>(dpp_add<0x122>(dpp_add<0x124>(dpp_add<0x128>(v))));
 }
 
 // Combine across the four 16-lane rows of a wave on the VALU.  v_permlane16_swap
@@ -106,76 +109,56 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---------------------------------------------------------------------------
 // Split merge inside one launch (flash-decoding without a second kernel)
 // ---------------------------------------------------------------------------
-// Each work-group of a (sequence, KV head) publishes an (max, sum, o) partial and
-// takes a ticket; the last arrival merges.  On a multi-XCD part a device-scope
-// __threadfence() writes back and invalidates the whole L2 of the issuing XCD, which
-// costs far more than the partials themselves when every work-group does it.  The
-// partials are therefore written and read with agent-scope relaxed atomics (per-access
-// write-through / L2-bypassing, coherent across XCDs), the writer waits for its stores
-// to complete (s_waitcnt vmcnt(0)) before the ticket is taken, and the reader loads
-// only after the ticket told it everyone else had arrived.
-//   MASW_SPLIT_MERGE 2: that protocol (default);
-//   MASW_SPLIT_MERGE 1: plain stores/loads with __threadfence() around the ticket;
-//   MASW_SPLIT_MERGE 0: the decode kernel does not merge in-launch, a separate combine
-//                       kernel follows it; the other in-launch merges (the projection's
-//                       hidden slices) keep the protocol of 2.
-#ifndef MASW_SPLIT_MERGE
-#define MASW_SPLIT_MERGE 2
-#endif
+// Work-groups of one unit exchange partial results through memory.  On a multi-XCD
+// part a device-scope __threadfence() writes back and invalidates the whole L2 of the
+// issuing XCD, which costs far more than the partials themselves, so partials are
+// written and read with agent-scope relaxed atomics (per-access write-through /
+// L2-bypassing, coherent across XCDs).  Two protocols use them:
+//  - ticket after data (the projection's hidden slices): every work-group stores its
+//    partial, waits for the stores (s_waitcnt vmcnt(0)), then takes a ticket
+//    (split_arrive); the last arrival loads the others' partials;
+//  - self-validating partials (the decode kernel, decode_attn.hip): partials are stored
+//    encoded so that an unwritten (zero) slot is recognisable and the ticket need not
+//    wait for the data.
 
 __device__ __forceinline__ void store_partial(float* p, float v) {
-#if MASW_SPLIT_MERGE != 1
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  *p = v;
-#endif
 }
 
 __device__ __forceinline__ float load_partial(const float* p) {
-#if MASW_SPLIT_MERGE != 1
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  return *p;
-#endif
 }
 
-// Two adjacent partial values (an 8-byte aligned pair) as one 64-bit access.
+// Two adjacent 32-bit words (an 8-byte aligned pair) as one 64-bit access.
+__device__ __forceinline__ void store_word2(void* p, uint32_t w0, uint32_t w1) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), (uint64_t(w1) << 32) | w0, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ u32x2_t load_word2(const void* p) {
+  const uint64_t w = __hip_atomic_load(static_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x2_t{uint32_t(w), uint32_t(w >> 32)};
+}
+
 __device__ __forceinline__ void store_partial2(float* p, float v0, float v1) {
-  const uint64_t w = (uint64_t(__float_as_uint(v1)) << 32) | __float_as_uint(v0);
-#if MASW_SPLIT_MERGE != 1
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  *reinterpret_cast<uint64_t*>(p) = w;
-#endif
+  store_word2(p, __float_as_uint(v0), __float_as_uint(v1));
 }
 
 __device__ __forceinline__ float2 load_partial2(const float* p) {
-#if MASW_SPLIT_MERGE != 1
-  const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  const uint64_t w = *reinterpret_cast<const uint64_t*>(p);
-#endif
-  return make_float2(__uint_as_float(uint32_t(w)), __uint_as_float(uint32_t(w >> 32)));
+  const u32x2_t w = load_word2(p);
+  return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
 }
 
 // Called by every thread of the work-group after its partial stores; true (for the
 // whole work-group) when this is the last of n_valid arrivals.  The last arrival
 // resets the counter with reset_ticket() once it has merged.
 __device__ __forceinline__ bool split_arrive(int32_t* counter, int n_valid, int* sm_flag) {
-#if MASW_SPLIT_MERGE == 1
-  __threadfence();
-#else
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
-#endif
   __syncthreads();
   if (threadIdx.x == 0)
     *sm_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_valid - 1;
   __syncthreads();
-  const bool last = *sm_flag != 0;
-#if MASW_SPLIT_MERGE == 1
-  if (last) __threadfence();
-#endif
-  return last;
+  return *sm_flag != 0;
 }
 
 __device__ __forceinline__ void reset_ticket(int32_t* counter) {

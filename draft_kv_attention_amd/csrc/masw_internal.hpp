@@ -127,17 +127,7 @@ struct VerifyArgs {
 
 int launch_verify_mfma(const VerifyArgs& a, hipStream_t s);
 constexpr int kMaxVerifySplits = 64;   // splits the MFMA verifier merges (more are clamped)
-// MASW_VERIFY_STREAM 1: waves stream their own key ranges through private LDS stages
-// (verify_stream_kernel, one 128 KB work-group per CU); 0: work-group tiles staged
-// through registers (verify_kernel).
-#ifndef MASW_VERIFY_STREAM
-#define MASW_VERIFY_STREAM 1
-#endif
-constexpr bool kVerifyStream = MASW_VERIFY_STREAM != 0;
-// Verifier work-groups that stay resident per CU for `rows` = G * n_q query rows.  The
-// streaming kernel holds 128 KB of LDS: one per CU.  The register-staged kernel, measured
-// on 8B / 70B layer shares: 32-row blocks fill the chip best at one per CU, 64-row
-// blocks at two.
-inline int verify_resident_per_cu(int rows) { return kVerifyStream || rows <= 32 ? 1 : 2; }
+// Verifier work-groups resident per CU: the streaming kernel holds 128-150 KB of LDS.
+inline int verify_resident_per_cu(int /*rows*/) { return 1; }
 
 }  // namespace masw

@@ -15,16 +15,11 @@
 // layout (lane = row, registers = keys) is the B-operand layout the second product
 // needs, with its 32 keys taken in the order the registers hold them.
 //
-// Work-group = 4 waves over one (split, KV head, sequence); two kernels implement it.
-// verify_stream_kernel (the default, further down) lets every wave stream its own key
-// range through private LDS stages.  verify_kernel (MASW_VERIFY_STREAM=0, the earlier
-// design) stages a tile of 32*4/NB keys of K and V per iteration for the whole
-// work-group (272-byte padded rows: conflict-free 16-byte row reads and 2-byte column
-// reads); wave w owns row block w / (4/NB) and the 32-key slice w % (4/NB) of the tile,
-// so each wave keeps one 64-float O^T accumulator, and the next tile's global loads are
-// issued into registers before the current tile is computed.  In both the waves merge
-// through LDS in a fixed order; the splits are merged by a combine pass launched right
-// after (verify_combine_kernel).
+// Work-group = 4 waves over one (split, KV head, sequence): every wave streams its own
+// key range through private LDS stages (verify_stream_kernel); the waves merge through
+// LDS in a fixed order, and the splits are merged by a combine pass launched right after
+// (verify_combine_kernel).
+
 #include "masw_internal.hpp"
 
 namespace masw {
@@ -32,237 +27,20 @@ namespace {
 
 constexpr int kVWaves = 4;
 constexpr int kVThreads = kVWaves * kWave;
-constexpr int kRS = 136;       // LDS row stride in bf16 elements (272 bytes)
+constexpr int kRS = 136;       // LDS row stride of the staged queries in bf16 elements (272 bytes)
 constexpr int kD = 128;
 constexpr int kMaxRows = 64;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int NB> struct VTile {
-  static constexpr int WPR = kVWaves / NB;      // waves per row block
-  static constexpr int TK = 32 * WPR;           // keys per work-group tile
-  static constexpr int PER_THREAD = TK * 16 / kVThreads;   // 16-byte K chunks per thread
-};
-
 __device__ __forceinline__ int verify_chunk(int n, int n_splits, int tk) {
   int c = (n + n_splits - 1) / n_splits;
   return (c + tk - 1) / tk * tk;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
-}
-
-// Global K/V rows of one tile into registers: 16 lanes per 256-byte row.
-template <int PT>
-__device__ __forceinline__ void fetch_tile(u32x4_t (&kr)[PT], u32x4_t (&vr)[PT], const uint16_t* kbase,
-                                           const uint16_t* vbase, int tile, int k1) {
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int c = i * kVThreads + threadIdx.x;   // chunk id inside the tile
-    const int key = min(tile + (c >> 4), k1 - 1);
-    kr[i] = *reinterpret_cast<const u32x4_t*>(kbase + size_t(key) * kD + (c & 15) * 8);
-    vr[i] = *reinterpret_cast<const u32x4_t*>(vbase + size_t(key) * kD + (c & 15) * 8);
-  }
-}
-
-template <int PT>
-__device__ __forceinline__ void stage_tile(const u32x4_t (&kr)[PT], const u32x4_t (&vr)[PT], uint16_t* Kt, uint16_t* Vt) {
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int c = i * kVThreads + threadIdx.x;
-    *reinterpret_cast<u32x4_t*>(Kt + (c >> 4) * kRS + (c & 15) * 8) = kr[i];
-    *reinterpret_cast<u32x4_t*>(Vt + (c >> 4) * kRS + (c & 15) * 8) = vr[i];
-  }
-}
-
-// Partial / output row of query row `row` (= g * n_q + j) of KV head kvh.
-__device__ __forceinline__ size_t verify_prow(const VerifyArgs& a, int b, int kvh, int row) {
-  const int G = a.Hq / a.Hkv;
-  const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
-  return (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
-}
-
-template <int NB>
-__global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyArgs a) {
-  constexpr int WPR = VTile<NB>::WPR;
-  constexpr int TK = VTile<NB>::TK;
-  constexpr int PT = VTile<NB>::PER_THREAD;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int rb = wave / WPR;                  // row block of this wave
-  const int kslice = (wave % WPR) * 32;       // key slice of this wave inside a tile
-  const int G = a.Hq / a.Hkv;
-  const int R = G * a.n_q;
-  const int l32 = lane & 31, half = lane >> 5;
-
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[NB * 32 * kRS];
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * TK * kRS];
-  uint16_t* Kt = sKV;
-  uint16_t* Vt = sKV + TK * kRS;
-
-  const int t = a.seq_len[b];
-  // Q rows of this KV head into LDS (rows >= R are zero).
-  for (int c = threadIdx.x; c < NB * 32 * 16; c += kVThreads) {
-    const int row = c >> 4, ch = c & 15;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (row < R) {
-      const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
-      v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) +
-                                            ((size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g) * kD + ch * 8);
-    }
-    *reinterpret_cast<u32x4_t*>(sQ + row * kRS + ch * 8) = v;
-  }
-  if (t < a.n_q || t > a.max_len) {
-    if (split == 0 && kvh == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SEQ_RANGE);
-    return;
-  }
-  const int n = t;
-  const int chunk = verify_chunk(n, a.n_splits, TK);
-  const int k0 = split * chunk;
-  if (k0 >= n) return;
-  const int k1 = min(k0 + chunk, n);
-  const int n_valid = (n + chunk - 1) / chunk;
-
-  // causal limit of this lane's row: last key row (0-based) query j may see
-  const int rho = rb * 32 + l32;
-  const int lim = rho < R ? t - a.n_q + (rho - (rho / a.n_q) * a.n_q) : -1;
-
-  const size_t unit = size_t(b) * a.Hkv + kvh;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + unit * a.max_len * kD;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + unit * a.max_len * kD;
-
-  f32x16_t o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
-  u32x4_t kr[PT], vr[PT];
-  fetch_tile<PT>(kr, vr, kbase, vbase, k0, k1);
-  for (int tile = k0; tile < k1; tile += TK) {
-    __syncthreads();                  // previous tile fully consumed (and Q staged)
-    stage_tile<PT>(kr, vr, Kt, Vt);
-    __syncthreads();
-    if (tile + TK < k1) fetch_tile<PT>(kr, vr, kbase, vbase, tile + TK, k1);   // next tile in flight
-
-    const int key0 = tile + kslice;
-    if (key0 < k1) {
-      f32x16_t s;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(Kt + (kslice + l32) * kRS + ks * 16 + half * 8);
-        const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(sQ + (rb * 32 + l32) * kRS + ks * 16 + half * 8);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
-                                                    __builtin_bit_cast(bf16x8_t, bq), s, 0, 0, 0);
-      }
-      // S^T layout: register v holds key 8*(v/4) + 4*half + v%4 of the slice, row l32.
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + 8 * (v >> 2) + 4 * half + (v & 3);
-        const float sc = (key < k1 && key <= lim) ? s[v] * a.scale_log2 : -INFINITY;
-        s[v] = sc;
-        tmax = fmaxf(tmax, sc);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float mn = fmaxf(m, tmax);
-      const float mref = mn == -INFINITY ? 0.f : mn;   // a row may have no key in this slice
-      const float alpha = fast_exp2(m - mref);
-      if (__any(mn != m)) {          // rescale only when some row's max grew
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      }
-      m = mn;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(s[v] - mref);
-        s[v] = p;
-        l += p;
-      }
-      // O^T += V^T P^T, two k-steps of 16 keys in register order.
-#pragma unroll
-      for (int step = 0; step < 2; ++step) {
-        const int v0 = 8 * step;
-        const u32x4_t pb = {pack_bf16x2(s[v0 + 0], s[v0 + 1]), pack_bf16x2(s[v0 + 2], s[v0 + 3]),
-                            pack_bf16x2(s[v0 + 4], s[v0 + 5]), pack_bf16x2(s[v0 + 6], s[v0 + 7])};
-        const int kb = kslice + 16 * step + 4 * half;   // keys kb..kb+3, kb+8..kb+11
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const uint16_t* vc = Vt + db * 32 + l32;
-          const u32x4_t af = {uint32_t(vc[(kb + 0) * kRS]) | (uint32_t(vc[(kb + 1) * kRS]) << 16),
-                              uint32_t(vc[(kb + 2) * kRS]) | (uint32_t(vc[(kb + 3) * kRS]) << 16),
-                              uint32_t(vc[(kb + 8) * kRS]) | (uint32_t(vc[(kb + 9) * kRS]) << 16),
-                              uint32_t(vc[(kb + 10) * kRS]) | (uint32_t(vc[(kb + 11) * kRS]) << 16)};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
-                                                          __builtin_bit_cast(bf16x8_t, pb), o[db], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // Keys of a row are split between lanes l32 and l32 + 32: total their sums.
-  l += __shfl_xor(l, 32, kWave);
-
-  // Merge the waves of each row block in a fixed order through LDS (reusing the tiles).
-  __syncthreads();
-  float* sm_ml = reinterpret_cast<float*>(sKV);          // [waves][32 rows][2]
-  float* sm_o = sm_ml + kVWaves * 32 * 2;                 // [NB*32 rows][128]
-  if (half == 0) {
-    sm_ml[(wave * 32 + l32) * 2] = m;
-    sm_ml[(wave * 32 + l32) * 2 + 1] = l;
-  }
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < WPR; ++w) M = fmaxf(M, sm_ml[((rb * WPR + w) * 32 + l32) * 2]);
-  const float wt = fast_exp2(m - (M == -INFINITY ? 0.f : M));
-  for (int w = 0; w < WPR; ++w) {
-    if (wave % WPR == w) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int idx = (rb * 32 + l32) * kD + db * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const float val = wt * o[db][v];
-          sm_o[idx] = w == 0 ? val : sm_o[idx] + val;
-        }
-    }
-    __syncthreads();
-  }
-
-  uint16_t* out = static_cast<uint16_t*>(a.out);
-  for (int idx = threadIdx.x; idx < R * kD; idx += kVThreads) {
-    const int row = idx / kD, d = idx - (idx / kD) * kD;
-    const int rblk = row >> 5, r32 = row & 31;
-    const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
-    const size_t prow = (size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g;
-    float Mr = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < WPR; ++w) Mr = fmaxf(Mr, sm_ml[((rblk * WPR + w) * 32 + r32) * 2]);
-    const float Mrr = Mr == -INFINITY ? 0.f : Mr;
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < WPR; ++w)
-      L = fmaf(fast_exp2(sm_ml[((rblk * WPR + w) * 32 + r32) * 2] - Mrr), sm_ml[((rblk * WPR + w) * 32 + r32) * 2 + 1], L);
-    const float O = sm_o[row * kD + d];
-    if (n_valid == 1) {
-      out[prow * kD + d] = f32_to_bf16(O / L);
-    } else {
-      const size_t pr = prow * a.n_splits + split;
-      store_partial(&a.part_o[pr * kD + d], O);
-      if (d == 0) { store_partial(&a.part_ml[pr * 2], Mr); store_partial(&a.part_ml[pr * 2 + 1], L); }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Streaming variant (default): every wave owns a contiguous key range of the split and
+// Every wave owns a contiguous key range of the split and
 // streams it through two private LDS stages filled by asynchronous global->LDS copies,
 // so the loop has no work-group barrier and two 32-key tiles (32 KB) per wave stay in
 // flight while the matrix cores work on the current one.
@@ -605,25 +383,14 @@ __global__ __launch_bounds__(kCombRows * 64) void verify_combine_kernel(const Ve
 
 int launch_verify_mfma(const VerifyArgs& a, hipStream_t s) {
   const int rows = a.Hq / a.Hkv * a.n_q;
-  int tk;
-  if (kVerifyStream) {
-    if (rows <= 32) {
-      hipLaunchKernelGGL(verify_stream_kernel<1>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
-    } else if (rows <= kMaxRows) {
-      hipLaunchKernelGGL(verify_stream_kernel<2>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
-    } else {
-      return MASW_ERR_SHAPE;
-    }
-    tk = kVSplitRound;
-  } else if (rows <= 32) {
-    hipLaunchKernelGGL(verify_kernel<1>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
-    tk = VTile<1>::TK;
+  if (rows <= 32) {
+    hipLaunchKernelGGL(verify_stream_kernel<1>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
   } else if (rows <= kMaxRows) {
-    hipLaunchKernelGGL(verify_kernel<2>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
-    tk = VTile<2>::TK;
+    hipLaunchKernelGGL(verify_stream_kernel<2>, dim3(a.n_splits, a.Hkv, a.B), dim3(kVThreads), 0, s, a);
   } else {
     return MASW_ERR_SHAPE;
   }
+  const int tk = kVSplitRound;
   if (a.n_splits > 1)
     hipLaunchKernelGGL(verify_combine_kernel, dim3((a.n_q * a.Hq + kCombRows - 1) / kCombRows, a.B), dim3(kCombRows * 64),
                        0, s, a, tk);

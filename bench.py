@@ -209,6 +209,14 @@ class Stack:
         return self.L * (self.attn_bytes(t) + self.shape.batch * self.kv_row_bytes())
 
 
+def first_boundary_after(t, S, W, r):
+    """The first slot-boundary position > t (r = 0: none)."""
+    if not r:
+        return None
+    d = max(t + 1 - S - W, r)
+    return S + W + -(-d // r) * r
+
+
 def time_steps(stack, which, t_start, warmup, steps, quantiles=False):
     """Replay `steps` graph steps from position t_start after `warmup` untimed ones.
     Returns (mean ms per step, mean algorithmic bytes per step) and, with quantiles,
@@ -218,6 +226,7 @@ def time_steps(stack, which, t_start, warmup, steps, quantiles=False):
     for _ in range(warmup):
         rep()
     t0 = stack.t
+    stack.timed_positions = (t0 + 1, t0 + steps)
     torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record()
@@ -598,44 +607,100 @@ def materialize_leg(stack, t_boundary, replays=5, dims=None, ws=None):
               + stack.attn_bytes(keys) * B // sh.batch + B * stack.kv_row_bytes())
     return dict(batch=B, slot_index=m, us_per_layer=round(per_layer, 2), bytes_per_layer=int(nbytes),
                 gbs=round(nbytes / per_layer / 1e3, 1), per_decode_step_us=round(per_layer * L / stack.r, 2),
-                slots_after=int(stack.layers[0].n_slots[0].item()))
+                slots_after=int(stack.layers[0].n_slots[0].item()), device_err_bits=int(seq.err.item()))
 
 
-def cpu_baseline(budget_s=15.0):
-    """The fp64 oracle's decode over the same memory shape, on the host, single thread.
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
-    Sample: (layer, sequence) units of the 3B-shaped MASW decode at prefix 32768 (one
-    query per q head over keylist(t)), repeated until ~budget_s; scaled to steps/s of
-    the 28-layer, 8-sequence step.
-    """
-    from threadpoolctl import threadpool_limits
+
+def _oracle_sample(seed):
+    """Seeded memory of one (layer, sequence) unit at prefix 32768: its K/V rows gathered
+    into the key order of the MASW memory (and of the full cache), and queries."""
     from oracle import masw_oracle as O
     sh = SHAPE
-    S, W, r, Hkv, D = sh.sink, sh.window, sh.interval, sh.n_kv_heads, sh.head_dim
+    S, W, r, Hq, Hkv, D = sh.sink, sh.window, sh.interval, sh.n_q_heads, sh.n_kv_heads, sh.head_dim
     t = T_HEAD
-    rng = np.random.default_rng(0)
+    rng = np.random.default_rng(seed)
     n = O.visible_slot_count(t, S, W, r)
     raw_k = rng.standard_normal((t + 1, Hkv, D), dtype=np.float32)
     raw_v = rng.standard_normal((t + 1, Hkv, D), dtype=np.float32)
     slot_k = rng.standard_normal((n + 1, Hkv, D), dtype=np.float32)
     slot_v = rng.standard_normal((n + 1, Hkv, D), dtype=np.float32)
-    scale = O.default_scale(D)
-    units = 0
+    keys = O.keylist(t, S, W, r)
+    g0 = time.perf_counter()
+    ks = np.stack([raw_k[i] if kind == "raw" else slot_k[i] for kind, i in keys], axis=1).astype(np.float64)
+    vs = np.stack([raw_v[i] if kind == "raw" else slot_v[i] for kind, i in keys], axis=1).astype(np.float64)
+    gather_s = time.perf_counter() - g0
+    return dict(ks=ks, vs=vs, raw_k=raw_k, raw_v=raw_v, qs=rng.standard_normal((64, Hq, D)),
+                scale=O.default_scale(D), keys=len(keys), gather_s=gather_s)
+
+
+def _oracle_time(seed, seconds):
+    """(units, seconds) of the oracle's gqa_attend on one unit's gathered rows, repeated
+    for about `seconds`, BLAS on one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import masw_oracle as O
+    smp = _oracle_sample(seed)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            keys = O.keylist(t, S, W, r)
-            ks = np.stack([raw_k[i] if kind == "raw" else slot_k[i] for kind, i in keys], axis=1)
-            vs = np.stack([raw_v[i] if kind == "raw" else slot_v[i] for kind, i in keys], axis=1)
-            q = rng.standard_normal((sh.n_q_heads, D))
-            O.gqa_attend(q, ks.astype(np.float64), vs.astype(np.float64), scale)
-            units += 1
-        el = time.perf_counter() - t0
-    per_step = el / units * sh.layers * sh.batch
-    return dict(value=round(1.0 / per_step, 5), unit="steps/s", cores=1, kind="oracle",
-                sample=f"{units} (layer, sequence) MASW decode units at prefix {t} "
-                       f"({len(O.keylist(t, S, W, r))} keys, 24 q heads) in {el:.1f} s, "
-                       f"scaled x{sh.layers * sh.batch} to one 28-layer batch-8 step")
+        done = 0
+        while time.perf_counter() - t0 < seconds:
+            O.gqa_attend(smp["qs"][done % 64], smp["ks"], smp["vs"], smp["scale"])
+            done += 1
+        return done, time.perf_counter() - t0
+
+
+def cpu_baseline(seconds=3.0, full_units=2):
+    """The fp64 oracle's decode on the host cores, on the same memory shapes.
+
+    Sample: (layer, sequence) units of the 3B-shaped MASW decode at prefix 32768 - one
+    query per q head, the oracle's own gqa_attend on key/value rows gathered beforehand
+    (the gather is timed separately) - on one core for `seconds`, then on `procs` cores
+    at once (one process per core, forked before the GPU is touched, each with its own
+    seeded memory, seconds / 2 each).  Scaled to steps/s of the 28-layer, 8-sequence
+    step.  The full-KV baseline (32768 keys per unit) is timed on `full_units` units on
+    one core and scaled the same way (an extrapolation: ~90 GFLOP per step).
+    """
+    import multiprocessing
+    from threadpoolctl import threadpool_limits
+    from oracle import masw_oracle as O
+    sh = SHAPE
+    units_per_step = sh.layers * sh.batch
+    procs = max(1, min(16, len(os.sched_getaffinity(0))))
+    single, el1 = _oracle_time(0, seconds)
+    with multiprocessing.get_context("fork").Pool(procs) as pool:
+        parts = pool.starmap(_oracle_time, [(1 + i, seconds / 2) for i in range(procs)])
+    multi = sum(p[0] for p in parts)
+    eln = max(p[1] for p in parts)
+    smp = _oracle_sample(0)
+    kf = smp["raw_k"][1:T_HEAD + 1].transpose(1, 0, 2).astype(np.float64)
+    vf = smp["raw_v"][1:T_HEAD + 1].transpose(1, 0, 2).astype(np.float64)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for i in range(full_units):
+            O.gqa_attend(smp["qs"][i], kf, vf, smp["scale"])
+        elf = time.perf_counter() - t0
+    per_step_1 = el1 / single * units_per_step
+    per_step_n = eln / multi * units_per_step
+    per_step_full = elf / full_units * units_per_step
+    return dict(value=round(1.0 / per_step_n, 5), unit="steps/s", cores=procs, kind="oracle",
+                sample=f"{multi} (layer, sequence) MASW decode units at prefix {T_HEAD} ({smp['keys']} keys, "
+                       f"{sh.n_q_heads} q heads) on {procs} cores in {eln:.1f} s, scaled x{units_per_step} to one "
+                       f"28-layer batch-8 step; key/value rows gathered beforehand",
+                cpu_model=_cpu_model(), host_cpus=os.cpu_count(),
+                single_core=dict(value=round(1.0 / per_step_1, 5), units=single, seconds=round(el1, 2)),
+                gather_s_per_unit=round(smp["gather_s"], 4),
+                fullkv=dict(value=round(1.0 / per_step_full, 6), unit="steps/s", cores=1, units=full_units,
+                            seconds=round(elf, 2), keys=T_HEAD, extrapolated=True,
+                            note=f"{full_units} full-KV units timed on one core, scaled x{units_per_step}"))
 
 
 def profile_modes(args, dev):
@@ -685,9 +750,15 @@ def main():
         print("bench.py runs on one GPU only: the draft path shards by sequence or KV head "
               "without communication, so a multi-GPU figure is not produced", file=sys.stderr)
         sys.exit(2)
+    sh = SHAPE
+    plain = not (args.roofline_only or args.traffic_probe or args.prefill_only)
+    cpu = None
+    if plain and not args.no_cpu:
+        # first, before anything touches the GPU: the oracle's worker processes are forked
+        cpu = cpu_baseline()
+        print(f"[bench] cpu baseline {cpu}", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     M.lib()
-    sh = SHAPE
     if args.roofline_only or args.traffic_probe:
         profile_modes(args, dev)
         return
@@ -702,11 +773,19 @@ def main():
     stack.capture()
     print("[bench] graphs captured", file=sys.stderr, flush=True)
 
-    # headline: MASW at prefix 32768
-    ms, nbytes, head_q = time_steps(stack, "masw", T_HEAD, args.warmup, args.steps, quantiles=True)
+    # headline: MASW at prefix 32768.  The timed window starts on the first slot boundary
+    # after the prefix (the warm-up steps end just before it), so it holds
+    # ceil(steps / r) boundary steps: the materialization cost is inside the headline
+    # at least at its steady-state rate (exactly, when steps is a multiple of r).
+    b0 = first_boundary_after(T_HEAD, sh.sink, sh.window, sh.interval)
+    head_start = b0 - 1 - args.warmup
+    ms, nbytes, head_q = time_steps(stack, "masw", head_start, args.warmup, args.steps, quantiles=True)
+    lo, hi = stack.timed_positions
+    n_bound = sum(1 for t in range(lo, hi + 1) if is_boundary(t, sh.sink, sh.window, sh.interval))
     value = 1e3 / ms
     gbs = nbytes / (ms * 1e-3) / 1e9
-    print(f"[bench] MASW t={T_HEAD}: {ms:.3f} ms/step {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"[bench] MASW prefix {T_HEAD}: positions {lo}..{hi} ({n_bound} boundary steps): "
+          f"{ms:.3f} ms/step {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
     sweep = []
     if not args.no_sweep:
@@ -734,7 +813,6 @@ def main():
 
     roof = kernel_roofline(stack, T_HEAD)
     print(f"[bench] roofline {roof}", file=sys.stderr, flush=True)
-    err_bits = int(stack.seq.err.item()) | int(stack.err_full.item())
     mat = materialize_leg(stack, 2052 + 480 * 64)
     mat_rope = materialize_leg(stack, 2052 + 480 * 64,
                                dims=dataclasses.replace(stack.d, rope_theta=500000.0, rope_style=M.ROPE_ROTATE_HALF))
@@ -746,6 +824,7 @@ def main():
     ws4 = M.workspace(d4, M.OP_MATERIALIZE, device=dev)
     mat["batch4"] = {m: materialize_leg(stack, 2052 + m * 64, dims=d4, ws=ws4) for m in (1, 480)}
     print(f"[bench] materialization {mat}", file=sys.stderr, flush=True)
+    err_bits = int(stack.seq.err.item()) | int(stack.err_full.item())   # every leg on the stack
     del stack
     torch.cuda.empty_cache()
     ver = verify_leg(dev)
@@ -764,10 +843,6 @@ def main():
     mref = mfma_reference_leg(dev)
     print(f"[bench] matrix-core reference {mref}", file=sys.stderr, flush=True)
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline()
-        print(f"[bench] cpu baseline {cpu}", file=sys.stderr, flush=True)
 
     full_head = next((r for r in sweep if r["prefix"] == T_HEAD), None)
     line = {
@@ -780,6 +855,7 @@ def main():
                    "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "sink": sh.sink,
                    "window": sh.window, "interval": sh.interval},
         "ms_per_step_p10_p50_p90": head_q,
+        "timed_positions": [lo, hi], "boundary_steps_timed": n_bound,
         "hbm_gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(value * sh.batch, 1),
         "fullkv_at_prefix": full_head, "sweep": sweep, "eq3_fit": fits, "device_err_bits": err_bits,

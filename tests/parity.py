@@ -53,13 +53,47 @@ def assert_close(gpu, ref, dtype, what=""):
     return s
 
 
-def slot_bound(h, w, n_kv_heads, head_dim):
-    """Per-element allowance for a stored slot K/V (the bf16 rounding of an fp32 sum
-    H W_g): the forward error bound of an fp32 dot product of length n in any summation
-    order, n * 2^-24 * sum_k |h_k w_k|, shaped [..., Hkv, D].  It is added to one bf16 ulp
-    of the oracle's rounded fp64 value; it matters only where the sum cancels."""
+def proj_sum_depth(hidden, prefill=False):
+    """Longest chain of fp32 additions one product h_k w_kn passes through in the bf16
+    slot projection (matrix cores): up to 32 inside the 16x16x32 MFMA that forms it (the
+    hardware's own order is not documented, so a sequential chain is assumed), one per
+    further MFMA step of its wave's hidden range, 4 for the sum of the work-group's waves
+    and one per hidden slice.  A boundary projection cuts the hidden size into at most 8
+    slices of a multiple of 128 rows; a prefill projection takes it whole.  Each slice's
+    rows are split between 4 waves in steps of 32."""
+    if prefill:
+        per, splits = -(-hidden // 128) * 128, 1
+    else:
+        per = -(-(-(-hidden // 8)) // 128) * 128
+        splits = -(-hidden // per)
+    steps = per // 4 // 32
+    return 32 + steps + 4 + splits
+
+
+def slot_bound(h, w, n_kv_heads, head_dim, prefill=False):
+    """Per-element allowance for a stored bf16 slot K/V (the bf16 rounding of an fp32 sum
+    H W_g) beyond one bf16 ulp of the oracle's rounded fp64 value: the forward error bound
+    of fp32 summation, depth * 2^-24 * sum_k |h_k w_k|, with depth the kernel's longest
+    addition chain (proj_sum_depth), shaped [..., Hkv, D].  It matters only where the sum
+    cancels."""
     h, w = np.abs(np.asarray(h, np.float64)), np.abs(np.asarray(w, np.float64))
-    return (h.shape[-1] * 2.0 ** -24 * (h @ w)).reshape(h.shape[:-1] + (n_kv_heads, head_dim))
+    depth = proj_sum_depth(h.shape[-1], prefill)
+    return (depth * 2.0 ** -24 * (h @ w)).reshape(h.shape[:-1] + (n_kv_heads, head_dim))
+
+
+def assert_slot_close(got, ref, bound, what=""):
+    """Stored bf16 slot K/V against the oracle's rounded value: every element within one
+    bf16 ulp plus the fp32 summation bound, and at least 99.9% of the elements within one
+    ulp outright (both roundings of a sum agree unless it sits near a rounding boundary)."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    ulp = bf16_ulp(ref)
+    err = np.abs(got - ref)
+    ulps = err / ulp
+    within1 = float((err <= ulp).mean())
+    msg = f"{what}: max {ulps.max():.2f} ulp, {100 * within1:.3f}% within 1 ulp"
+    assert (err <= ulp + bound).all(), msg
+    assert within1 >= 0.999, msg
+    return float(ulps.max())
 
 
 def bf16_ulp(x):
@@ -73,11 +107,11 @@ def rope_partner(D, style):
     return np.arange(D) ^ (D // 2 if style == 0 else 1)
 
 
-def rotated_slot_bound(h, w, n_kv_heads, head_dim, style, ref):
-    """Allowance for a rotated slot key: the fp32 dot-product bound of both components
-    of its pair (each enters with a weight |cos|, |sin| <= 1) plus the fp32 rounding of
-    the turn itself (a few 2^-24 of |x_a| + |x_b|, taken from the reference)."""
-    b = slot_bound(h, w, n_kv_heads, head_dim)
+def rotated_slot_bound(h, w, n_kv_heads, head_dim, style, ref, prefill=False):
+    """Allowance for a rotated slot key: the fp32 summation bound of both components of
+    its pair (each enters with a weight |cos|, |sin| <= 1) plus the fp32 rounding of the
+    turn itself (a few 2^-24 of |x_a| + |x_b|, taken from the reference)."""
+    b = slot_bound(h, w, n_kv_heads, head_dim, prefill)
     p = rope_partner(head_dim, style)
     r = np.abs(np.asarray(ref, np.float64))
     return b + b[..., p] + 2.0 ** -21 * (r + r[..., p])

@@ -17,7 +17,7 @@ import draft_kv_attention_amd as M
 import seeded_inputs as SI
 from oracle import masw_oracle as O
 from tests.gpu_driver import LayerDriver, np_in, shape_of
-from tests.parity import assert_close, bf16_ulp, slot_bound
+from tests.parity import assert_close, assert_slot_close, slot_bound
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -179,8 +179,8 @@ def test_3b_layer_bf16_to_8192():
             for m in (1, 50, 95):
                 ref = mem.slots[m][which]
                 h = np_in(SI.slot_inputs(drv.shape, drv.seed, 0, O.boundary_step(m, S, W, r))[0][b])
-                allow = bf16_ulp(ref) + slot_bound(h.astype(np.float64), w, ref.shape[0], ref.shape[1])
-                assert (np.abs(got[b, :, m - 1] - ref) <= allow).all()
+                assert_slot_close(got[b, :, m - 1], ref, slot_bound(h.astype(np.float64), w, ref.shape[0], ref.shape[1]),
+                                  f"slot {'KV'[which]} b={b} m={m}")
 
 
 # ---------------------------------------------------------------------------

@@ -17,7 +17,7 @@ import draft_kv_attention_amd as M
 import seeded_inputs as SI
 from oracle import masw_oracle as O
 from tests.gpu_driver import np_in
-from tests.parity import assert_close, bf16_ulp, slot_bound as _slot_bound
+from tests.parity import assert_close, assert_slot_close, slot_bound
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,19 +28,6 @@ def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
     M.lib()
-
-
-def _ulp_close(got, ref, acc_bound=0.0):
-    """Within one bf16 ulp of the oracle's rounded value, plus the fp32 accumulation
-    bound where the projection cancels (|K_g| much smaller than sum |h w|)."""
-    ulp = bf16_ulp(ref) + acc_bound
-    bad = np.abs(got - ref) > ulp
-    if bad.any():
-        idx = np.argwhere(bad)[:6]
-        print("beyond 1 bf16 ulp:", int(bad.sum()), "of", bad.size,
-              [(tuple(int(x) for x in i), float(got[tuple(i)]), float(ref[tuple(i)]), float(ulp[tuple(i)])) for i in idx],
-              flush=True)
-    return not bad.any()
 
 
 def test_materialize_chain_3b_to_512_slots():
@@ -83,8 +70,8 @@ def test_materialize_chain_3b_to_512_slots():
             got_k = layer.k_slot[:, :, m - 1].double().cpu().numpy()
             got_v = layer.v_slot[:, :, m - 1].double().cpu().numpy()
             hn = np_in(h).astype(np.float64)
-            assert _ulp_close(got_k, kg, _slot_bound(hn, wk_n, Hkv, D)), f"slot K m={m}"
-            assert _ulp_close(got_v, vg, _slot_bound(hn, wv_n, Hkv, D)), f"slot V m={m}"
+            assert_slot_close(got_k, kg, slot_bound(hn, wk_n, Hkv, D), f"slot K m={m}")
+            assert_slot_close(got_v, vg, slot_bound(hn, wv_n, Hkv, D), f"slot V m={m}")
             # the slot query saw exactly S + W + (m - 1) keys
             assert len(O.slot_query_keylist(m, S, W, r)) == S + W + m - 1
     torch.cuda.synchronize()
@@ -176,8 +163,8 @@ def test_projection_hidden_splits_and_batch_groups(hidden, B):
         got_k = layer.k_slot[:, :, 0].double().cpu().numpy()
         got_v = layer.v_slot[:, :, 0].double().cpu().numpy()
         hn = np_in(h).astype(np.float64)
-        assert _ulp_close(got_k, kg, _slot_bound(hn, np_in(wk).astype(np.float64), Hkv, D))
-        assert _ulp_close(got_v, vg, _slot_bound(hn, np_in(wv).astype(np.float64), Hkv, D))
+        assert_slot_close(got_k, kg, slot_bound(hn, np_in(wk).astype(np.float64), Hkv, D), "slot K")
+        assert_slot_close(got_v, vg, slot_bound(hn, np_in(wv).astype(np.float64), Hkv, D), "slot V")
         assert torch.isfinite(o.float()).all()
         rows.append((layer.k_slot[:, :, 0].clone(), layer.v_slot[:, :, 0].clone()))
     assert torch.equal(rows[0][0], rows[1][0]) and torch.equal(rows[0][1], rows[1][1])

@@ -25,7 +25,7 @@ import draft_kv_attention_amd as M
 import seeded_inputs as SI
 from oracle import masw_oracle as O
 from tests.gpu_driver import np_in
-from tests.parity import assert_close, bf16_ulp, rotated_slot_bound, slot_bound
+from tests.parity import assert_close, assert_slot_close, bf16_ulp, rotated_slot_bound, slot_bound
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -105,11 +105,12 @@ class Prefill:
                 assert np.isnan(gs[n:]).all(), "slot rows past n(P) were written"
             # stored slot K/V: [Hkv][max_slots][D] -> [n][Hkv][D]
             for name, ref_kv, w in (("k_slot", sk, self.wkn), ("v_slot", sv, self.wvn)):
-                bound = slot_bound(self.hn[b, :n], w, sh.n_kv_heads, sh.head_dim)
+                bound = slot_bound(self.hn[b, :n], w, sh.n_kv_heads, sh.head_dim, prefill=True)
                 if self.rope and name == "k_slot":
-                    bound = rotated_slot_bound(self.hn[b, :n], w, sh.n_kv_heads, sh.head_dim, self.rope[1], ref_kv)
+                    bound = rotated_slot_bound(self.hn[b, :n], w, sh.n_kv_heads, sh.head_dim, self.rope[1], ref_kv,
+                                               prefill=True)
                 got_kv = getattr(self.layer, name)[b, :, :n].float().cpu().numpy().transpose(1, 0, 2)
-                assert (np.abs(got_kv - ref_kv) <= bf16_ulp(ref_kv) + bound).all(), name
+                assert_slot_close(got_kv, ref_kv, bound, f"{name} b={b}")
 
     def check_memory(self, b):
         sh, d = self.sh, self.d

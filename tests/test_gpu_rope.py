@@ -21,7 +21,7 @@ import draft_kv_attention_amd as M
 import seeded_inputs as SI
 from oracle import masw_oracle as O
 from tests.gpu_driver import LayerDriver, np_in
-from tests.parity import assert_close, bf16_ulp, rotated_slot_bound, slot_bound
+from tests.parity import assert_close, assert_slot_close, bf16_ulp, rotated_slot_bound, slot_bound
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -48,9 +48,9 @@ def _check_slot_rows(drv, m, tol_fp32=1e-5):
     hn = np_in(h).astype(np.float64)
     style = drv.d.rope_style
     kb = rotated_slot_bound(hn, drv.wk_np, drv.d.n_kv_heads, drv.d.head_dim, style, ref_k)
-    assert (np.abs(got_k - ref_k) <= bf16_ulp(ref_k) + kb).all(), f"rotated slot K m={m}"
+    assert_slot_close(got_k, ref_k, kb, f"rotated slot K m={m}")
     vb = slot_bound(hn, drv.wv_np, drv.d.n_kv_heads, drv.d.head_dim)
-    assert (np.abs(got_v - ref_v) <= bf16_ulp(ref_v) + vb).all(), f"slot V m={m}"
+    assert_slot_close(got_v, ref_v, vb, f"slot V m={m}")
 
 
 def _run_chain(shape, max_slots, t_end, style, theta, seed):
@@ -116,8 +116,8 @@ def test_rope_large_position_id(style):
     got_k = layer.k_slot[:, :, m - 1].double().cpu().numpy()
     got_v = layer.v_slot[:, :, m - 1].double().cpu().numpy()
     kb = rotated_slot_bound(hn, wkn, sh.n_kv_heads, sh.head_dim, style, kg)
-    assert (np.abs(got_k - kg) <= bf16_ulp(kg) + kb).all()
-    assert (np.abs(got_v - vg) <= bf16_ulp(vg) + slot_bound(hn, wvn, sh.n_kv_heads, sh.head_dim)).all()
+    assert_slot_close(got_k, kg, kb, "rotated slot K")
+    assert_slot_close(got_v, vg, slot_bound(hn, wvn, sh.n_kv_heads, sh.head_dim), "slot V")
     # the rotation matters at this id: the unrotated key is far off
     k0, _ = O.project_slot(hn, wkn, wvn, sh.n_kv_heads, sh.head_dim, True)
     assert np.abs(got_k - k0).max() > 10 * np.abs(got_k - kg).max()

@@ -76,6 +76,7 @@ _SIGS = {
                                      ctypes.c_int32, _P]),
     "masw_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
+    "masw_decode_step_static": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
     "fullkv_decode_step": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
                                           ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "fullkv_verify_attn": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32,
@@ -313,6 +314,23 @@ def masw_decode_step(d: Dims, layer: Layer, seq: Seq, k_new: torch.Tensor, v_new
     _ok("masw_decode_step", lib().masw_decode_step(
         ctypes.byref(dc), ctypes.byref(lc), ctypes.byref(sc), k_new.data_ptr(), v_new.data_ptr(), n,
         q.data_ptr(), out.data_ptr(), wp, wb, _stream(stream)))
+
+
+def masw_decode_step_static(d: Dims, layer: Layer, seq: Seq, k_new: torch.Tensor, v_new: torch.Tensor,
+                            q: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """masw_decode_step with the library's own fixed scratch instead of a workspace
+    (allocates nothing; calls overlapping on one GPU race)."""
+    _check_layer(d, layer)
+    _check_seq(d, seq)
+    n = k_new.shape[1]
+    for nm, t in (("k_new", k_new), ("v_new", v_new)):
+        _check(t, nm, (d.batch, n, d.n_kv_heads, d.head_dim), d.dtype)
+    for nm, t in (("q", q), ("out", out)):
+        _check(t, nm, (d.batch, d.n_q_heads, d.head_dim), d.dtype)
+    dc, lc, sc = d.c(), layer.c(), seq.c()
+    _ok("masw_decode_step_static", lib().masw_decode_step_static(
+        ctypes.byref(dc), ctypes.byref(lc), ctypes.byref(sc), k_new.data_ptr(), v_new.data_ptr(), n,
+        q.data_ptr(), out.data_ptr(), _stream(stream)))
 
 
 def _check_full(d: Dims, k, v, seq_len, err):

@@ -3,10 +3,15 @@
 // touches device memory or synchronizes; every call only enqueues on `stream`.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "masw_internal.hpp"
 
 using namespace masw;
+
+// Scratch of masw_decode_step_static: [tickets: MASW_STATIC_MAX_UNITS int32][partials].
+// Each GPU the library runs on holds its own copy (zero at load) until the process ends.
+static __device__ __align__(256) unsigned char scratch[MASW_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -270,6 +275,69 @@ MASW_API int masw_decode_step(const masw_dims* d, const masw_layer* L, const mas
   a.q = q;
   a.out = out;
   fill_common(a, d, splits, ws, p);
+  return launch_decode(a, d->dtype, d->head_dim, stream);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};   // device address of `scratch` per device, once looked up
+
+// Device address of this device's scratch copy (the array's name is a host-side stand-in
+// and must never reach a kernel), looked up on the first call on each device.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+MASW_API int masw_decode_step_static(const masw_dims* d, const masw_layer* L, const masw_seq* seq,
+                                     const void* k_new, const void* v_new, int32_t n_new, const void* q,
+                                     void* out, hipStream_t stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if ((st = check_layer(d, L))) return st;
+  if (!seq || !seq->seq_len || !seq->err || !q || !out || n_new < 0) return MASW_ERR_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return MASW_ERR_ARG;
+  if (!all_aligned16(q, out, k_new, v_new)) return MASW_ERR_ARG;
+  const int splits = choose_splits(d, masw_max_keys(d));
+  const size_t units = size_t(d->batch) * d->n_kv_heads;
+  const size_t rows = size_t(d->batch) * d->n_q_heads;
+  const size_t ticket_bytes = align_up(size_t(MASW_STATIC_MAX_UNITS) * sizeof(int32_t));
+  const size_t po = align_up(rows * splits * d->head_dim * sizeof(float));
+  const size_t pml = align_up(rows * splits * 2 * sizeof(float));
+  if (splits > 1 && (units > MASW_STATIC_MAX_UNITS || ticket_bytes + po + pml > MASW_STATIC_SCRATCH_BYTES))
+    return MASW_ERR_WORKSPACE;
+  char* base = static_cast<char*>(scratch_on_current_device());
+  if (!base) return MASW_ERR_LAUNCH;
+  DecodeArgs a{};
+  fill_masw_memory(a, d, L);
+  a.seq_len = seq->seq_len;
+  a.err = seq->err;
+  a.n_slots = L->n_slots;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.n_new = n_new;
+  a.q = q;
+  a.out = out;
+  a.B = d->batch;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.n_splits = splits;
+  a.scale_log2 = scale_log2(d);
+  a.qo_stride = long(d->n_q_heads) * d->head_dim;
+  a.counters = splits > 1 ? reinterpret_cast<int32_t*>(base) : nullptr;
+  a.part_o = splits > 1 ? reinterpret_cast<float*>(base + ticket_bytes) : nullptr;
+  a.part_ml = splits > 1 ? reinterpret_cast<float*>(base + ticket_bytes + po) : nullptr;
   return launch_decode(a, d->dtype, d->head_dim, stream);
 }
 

@@ -62,7 +62,7 @@ extern "C" {
 #endif
 
 #define MASW_API __attribute__((visibility("default")))
-#define MASW_ABI_VERSION 5
+#define MASW_ABI_VERSION 6
 
 /* ---- host status codes ------------------------------------------------------- */
 enum {
@@ -213,6 +213,26 @@ MASW_API int masw_decode_step(const masw_dims* dims, const masw_layer* layer, co
                               const void* k_new, const void* v_new, int32_t n_new, const void* q,
                               void* out, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* masw_decode_step without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The split partials and tickets live
+ * in a fixed scratch array inside the library, one copy per GPU, held until the process
+ * ends: MASW_STATIC_SCRATCH_BYTES in total, of which the tickets take the first
+ * MASW_STATIC_MAX_UNITS int32 words (one per sequence and KV head: batch * n_kv_heads
+ * must not exceed it) and the partials the rest (batch * n_q_heads * splits *
+ * (head_dim + 2) * 4 bytes for the call's split plan, the same plan masw_decode_step
+ * chooses).  A call whose plan does not fit returns MASW_ERR_WORKSPACE before anything
+ * is enqueued.  The tickets start at zero and every call leaves them at zero.  All calls
+ * on one GPU share that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results; serialize them.  The first call
+ * on a device looks up the scratch address for that device (hipGetSymbolAddress) and
+ * returns MASW_ERR_LAUNCH if that fails.  Otherwise exactly masw_decode_step. */
+#define MASW_STATIC_SCRATCH_BYTES (8u << 20)
+#define MASW_STATIC_MAX_UNITS 16384
+MASW_API int masw_decode_step_static(const masw_dims* dims, const masw_layer* layer, const masw_seq* seq,
+                                     const void* k_new, const void* v_new, int32_t n_new, const void* q,
+                                     void* out, hipStream_t stream);
 
 /* Rollback after verification ([TR] §3.3 Algorithm 2 step 6): the target accepted the
  * draft's candidates up to position t_acc = seq_len[b] (the caller has already set

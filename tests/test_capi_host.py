@@ -189,3 +189,19 @@ def test_workspace_sizes(lib):
 def test_status_strings(lib):
     for st in range(-6, 1):
         assert M.status_string(st) not in ("", "unknown status")
+
+
+def test_static_decode_step_rejects_plans_beyond_its_scratch(lib):
+    """masw_decode_step_static keeps its partials in a fixed scratch: a split plan whose
+    partials or tickets do not fit returns MASW_ERR_WORKSPACE before anything is
+    enqueued (and before the scratch is looked up on a device)."""
+    A = 1 << 20
+    layer, seq = M._Layer(A, A, A, A, A, A, A), M._Seq(A, A)
+    for kw in (dict(batch=64, n_q_heads=64, n_kv_heads=8, num_splits=256),    # partials too big
+               dict(batch=4096, n_q_heads=24, n_kv_heads=8, num_splits=2)):   # too many tickets
+        d = _dims(**kw)
+        assert lib.masw_decode_step_static(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq),
+                                           A, A, 1, A, A, None) == -4, kw
+    d = _dims()
+    assert lib.masw_decode_step_static(ctypes.byref(d), ctypes.byref(layer), ctypes.byref(seq),
+                                       A + 8, A, 1, A, A, None) == -1

@@ -43,7 +43,7 @@ import seeded_inputs as SI           # noqa: E402
 METRIC = "draft attn steps/s + HBM GB/s (% peak) vs prefix 1K-32K, MASW vs full-KV"
 # Counter summary of the dominant kernel (two rocprofv3 --pmc passes of --traffic-probe)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_b8_prefix32768_hbm_traffic.md")
-DECODE_SOURCES = ("decode_attn.hip", "decode_args.hpp", "masw_device.hpp")
+DECODE_SOURCES = ("decode_attn.hip", "decode_args.hpp", "masw_device.hpp", "masw_internal.hpp", "project_mfma.hpp")
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak (no sparsity)
 SHAPE = SI.SWEEP_3B

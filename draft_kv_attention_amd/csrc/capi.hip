@@ -60,11 +60,11 @@ int choose_splits(const masw_dims* d, long max_keys, int per_cu = kDecodeResiden
 long masw_max_keys(const masw_dims* d) { return long(d->sink) + d->window + d->max_slots + 1; }
 
 struct WsPlan {
-  size_t flags, counters, part_o, part_ml, proj_counters, proj_part, total;
+  size_t flags, counters, part_o, part_ml, proj_counters, proj_part, launch_done, total;
 };
 
 // [per-sequence flags][per-(sequence, KV head) split tickets][partial o][partial max/sum]
-// and, for materialization, [projection tickets][projection partial sums].
+// and, for materialization, [projection tickets][projection partial sums][launch ticket].
 WsPlan plan_workspace(const masw_dims* d, int splits, int rows_per_seq, bool projection = false) {
   WsPlan p;
   const size_t rows = size_t(d->batch) * rows_per_seq;
@@ -79,7 +79,8 @@ WsPlan plan_workspace(const masw_dims* d, int splits, int rows_per_seq, bool pro
   const size_t pc = projection ? groups * 2 * (N / 64) * sizeof(int32_t) : 0;
   p.proj_part = p.proj_counters + align_up(pc);
   const size_t pp = projection ? groups * 2 * kMaxProjectSplits * 16 * N * sizeof(float) : 0;
-  p.total = p.proj_part + align_up(pp);
+  p.launch_done = p.proj_part + align_up(pp);
+  p.total = p.launch_done + (projection ? kAlign : 0);
   return p;
 }
 
@@ -411,19 +412,38 @@ MASW_API int masw_materialize_slot(const masw_dims* d, const masw_layer* L, cons
   pa.rope_style = d->rope_style;
   pa.counters = reinterpret_cast<int32_t*>(base + p.proj_counters);
   pa.part = reinterpret_cast<float*>(base + p.proj_part);
-  if ((st = launch_project(pa, d->dtype, stream))) return st;
 
   DecodeArgs a{};
   fill_masw_memory(a, d, L);
   a.seq_len = seq->seq_len;
   a.err = seq->err;
-  a.active = active;
   a.n_slots_out = L->n_slots;
   a.back = d->interval;
   a.self_slot = include_self ? 1 : 0;
   a.q = q_slot;
   a.out = o_slot;
   fill_common(a, d, splits, ws, p);
+  if (d->dtype == MASW_BF16 && !include_self) {
+    // The slot query does not read the new slot: projection and query share one launch.
+    BoundaryArgs ba{};
+    ba.p = pa;
+    a.n_slots = L->n_slots;
+    a.gate_boundary = 1;
+    a.n_slots_out = nullptr;   // published once every work-group has read n_slots
+    ba.d = a;
+    ba.publish = L->n_slots;
+    ba.proj_x = d->n_kv_heads * d->head_dim / 64;
+    ba.n_proj = ba.proj_x * 2 * pa.ksplits * ((d->batch + 15) / 16);
+    const long n_wg = long(ba.n_proj) + long(splits) * d->n_kv_heads * d->batch;
+    if (n_wg > 0x7fffffffL) return MASW_ERR_SHAPE;
+    ba.n_wg = int(n_wg);
+    ba.done = reinterpret_cast<int32_t*>(base + p.launch_done);
+    return launch_boundary(ba, d->head_dim, stream);
+  }
+  // With include_self the query needs the projected slot: two launches, the query gated
+  // by the projection's per-sequence decision.
+  if ((st = launch_project(pa, d->dtype, stream))) return st;
+  a.active = active;
   return launch_decode(a, d->dtype, d->head_dim, stream);
 }
 

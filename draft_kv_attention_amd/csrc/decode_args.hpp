@@ -40,6 +40,7 @@ struct DecodeArgs {
   int32_t* err;
   const int32_t* n_slots;   // MASW decode: checked against n(t); null for a full cache
   const int32_t* active;    // slot-query mode: per-sequence slot index m (0 = skip)
+  int gate_boundary;        // slot-query mode without `active`: decide m from seq_len, n_slots
   int32_t* n_slots_out;     // slot-query mode: set to m once the query is written
   int back;                 // keys of keylist(t - back)
   int self_slot;            // slot-query mode: also attend to the new slot itself

@@ -34,7 +34,7 @@
 // trip is needed when t changes.  With a fused append the newest n_new raw tokens are
 // read straight from the caller's k_new/v_new and split 0 writes them into the memory
 // (rows no other work-group of this launch reads).
-#include "decode_args.hpp"
+#include "project_mfma.hpp"
 
 namespace masw {
 namespace {
@@ -43,7 +43,7 @@ namespace {
 // error bits are reported once per sequence when `report`).
 __device__ __forceinline__ int decode_keys(const DecodeArgs& a, int t, int have, int act,
                                            KeySpan& ks, bool report) {
-  if (a.active) {  // slot query of masw_materialize_slot: gated by the boundary decision
+  if (a.active || a.gate_boundary) {  // slot query of masw_materialize_slot: gated by the boundary decision
     if (act <= 0) return 0;
     ks = key_span(t - a.back, a.g);
     ks.nslot += a.self_slot;
@@ -520,8 +520,20 @@ __device__ __forceinline__ void groups_reduce_scatter(float (&acc)[G][EPL], int 
 #undef MASW_X
 }
 
+// LDS of one decode work-group: the tile stages of the pipeline (once a wave has left
+// its loop, its own stages hold its accumulators for the merge of the waves), the
+// waves' (max, sum) and the merge flag.
+template <int G>
+struct DecodeLds {
+  u32x4_t pipe[kWaves][kPipeStages][kPipeStageInstr * kWave];
+  float sm_m[kWaves][G], sm_l[kWaves][G];
+  int sm_last;
+};
+
+// The work of work-group (split, kvh, b), with its LDS in `lds`.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, const int split, const int kvh, const int b,
+                                            DecodeLds<G>& lds) {
   constexpr int LPR = RowLayout<T>::LPR;
   constexpr int RPI = kWave / LPR;               // rows per wave instruction
   constexpr int EPL = D / LPR;                   // elements per lane of one row
@@ -538,7 +550,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   static_assert(KI == kPipeStageInstr, "a stage holds exactly one tile");
   static_assert(kPipeStages == 2, "the wait below assumes two stages");
 
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int lgrp = lane / LPR;
@@ -551,7 +562,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   const int have_raw = (a.n_slots ? a.n_slots : a.seq_len)[b];
   const int act_raw = (a.active ? a.active : a.seq_len)[b];
   const int have = a.n_slots ? have_raw : 0;
-  const int act = a.active ? act_raw : 1;
+  const int act = a.active ? act_raw : (a.gate_boundary ? pending_slot(t, have, a.g) : 1);
   uint32_t qw[G][NW];
   const T* qb = static_cast<const T*>(a.q) + size_t(b) * a.qo_stride + size_t(kvh) * G * D + lsub * VEC;
 #pragma unroll
@@ -616,7 +627,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   // hold its (g, d) accumulators for the merge of the waves.
   constexpr int WAVE_O = kPipeStages * KI * kWave * 4;   // floats per wave
   static_assert(G * D <= WAVE_O, "a wave's stages hold its accumulators");
-  __shared__ u32x4_t pipe[kWaves][kPipeStages][KI * kWave];
+  auto& pipe = lds.pipe;
   float* const sm_o = reinterpret_cast<float*>(&pipe[0][0][0]);
 
   // Wave w streams keys [w0, w1) of the chunk, one tile at a time (the last one ragged).
@@ -660,8 +671,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   groups_reduce_scatter<LPR, G, EPL>(acc, lane);
   constexpr int NF = G * EPL / (kWave / LPR);   // accumulators a lane keeps
 
-  __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
-  __shared__ int sm_last;
+  auto& sm_m = lds.sm_m;
+  auto& sm_l = lds.sm_l;
+  int& sm_last = lds.sm_last;
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) { sm_m[wave][g] = m[g]; sm_l[wave][g] = l[g]; }
@@ -720,6 +732,44 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   }
 }
 
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
+  __shared__ DecodeLds<G> lds;
+  decode_body<T, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
+
+// One launch for a slot boundary of a bf16 layer ([TR] §3.2 Algorithm 1 steps 1-4): the
+// first n_proj work-groups project the slot hidden state (K_g, V_g into slot row m-1),
+// the others run the slot query over keylist(t - r) - it does not read the new slot, so
+// both run side by side - each sequence gated by its own boundary decision.  Every
+// work-group reads n_slots at its start; the last one to finish (a launch-wide ticket)
+// publishes n_slots = m for the sequences at their boundary and resets the ticket.
+template <int D, int G>
+__global__ __launch_bounds__(kDecodeThreads) void boundary_kernel(const BoundaryArgs a) {
+  __shared__ union {
+    DecodeLds<G> d;
+    proj::ProjectLds<1> p;
+  } lds;
+  __shared__ int sm_done;
+  const int id = blockIdx.x;
+  if (id < a.n_proj) {
+    proj::project_mfma_body<1>(a.p, id % a.proj_x, (id / a.proj_x) % 2, id / (2 * a.proj_x), lds.p);
+  } else {
+    const int q = id - a.n_proj, ns = a.d.n_splits, hk = a.d.Hkv;
+    decode_body<uint16_t, D, G>(a.d, q % ns, (q / ns) % hk, q / (ns * hk), lds.d);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sm_done = __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.n_wg - 1;
+  __syncthreads();
+  if (!sm_done) return;
+  for (int b = threadIdx.x; b < a.d.B; b += kDecodeThreads) {
+    const int m = pending_slot(a.d.seq_len[b], a.d.n_slots[b], a.d.g);
+    if (m) a.publish[b] = m;
+  }
+  if (threadIdx.x == 0) reset_ticket(a.done);
+}
+
 __global__ void keylist_kernel(const MemGeom g, const int32_t* seq_len, int back, int32_t* out,
                                int max_keys) {
   const int b = blockIdx.x;
@@ -760,7 +810,30 @@ int launch_group(const DecodeArgs& a, hipStream_t s) {
   }
 }
 
+template <int D, int G>
+int launch_boundary_typed(const BoundaryArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((boundary_kernel<D, G>), dim3(a.n_wg), dim3(kDecodeThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? MASW_OK : MASW_ERR_LAUNCH;
+}
+
+template <int D>
+int launch_boundary_group(const BoundaryArgs& a, hipStream_t s) {
+  switch (a.d.Hq / a.d.Hkv) {
+    case 1: return launch_boundary_typed<D, 1>(a, s);
+    case 2: return launch_boundary_typed<D, 2>(a, s);
+    case 3: return launch_boundary_typed<D, 3>(a, s);
+    case 4: return launch_boundary_typed<D, 4>(a, s);
+    case 6: return launch_boundary_typed<D, 6>(a, s);
+    case 8: return launch_boundary_typed<D, 8>(a, s);
+    default: return MASW_ERR_SHAPE;
+  }
+}
+
 }  // namespace
+
+int launch_boundary(const BoundaryArgs& a, int D, hipStream_t s) {
+  return D == 128 ? launch_boundary_group<128>(a, s) : launch_boundary_group<64>(a, s);
+}
 
 int launch_decode(const DecodeArgs& a, int dtype, int D, hipStream_t s) {
   if (dtype == MASW_BF16) return D == 128 ? launch_group<uint16_t, 128>(a, s) : launch_group<uint16_t, 64>(a, s);

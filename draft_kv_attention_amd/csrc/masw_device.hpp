@@ -225,6 +225,16 @@ __device__ __forceinline__ AppendFate append_fate(int i, int t, int have, const 
   return kAppendWrite;
 }
 
+// Slot index m whose boundary step is t ([TR] §3.2 Algorithm 1 step 1: g_m is
+// materialized at t = S + W + m r) when the memory holds exactly m - 1 slots and has room
+// for the m-th; 0 otherwise (no boundary, already done, out of order or out of room).
+__device__ __forceinline__ int pending_slot(int t, int have, const MemGeom& g) {
+  const int d = t - g.S - g.W;
+  if (g.r < 1 || d < g.r || d % g.r) return 0;
+  const int m = d / g.r;
+  return have == m - 1 && m <= g.max_slots ? m : 0;
+}
+
 struct KeyRef {
   int seg;  // 0 sink, 1 ring, 2 slot
   int row;  // row inside that segment's [rows][D] block

@@ -83,6 +83,19 @@ inline int project_splits(int hidden) {
 
 int launch_project(const ProjectArgs& a, int dtype, hipStream_t s);
 
+// One launch for a bf16 slot boundary: the projection's work-groups (grid proj_x x 2 x
+// proj_z, flattened) followed by the gated slot query's (splits x Hkv x B); `done` is a
+// workspace ticket (zero between calls) and `publish` (the layer's n_slots) receives m.
+struct BoundaryArgs {
+  ProjectArgs p;
+  DecodeArgs d;
+  int proj_x, n_proj, n_wg;
+  int32_t* done;
+  int32_t* publish;
+};
+
+int launch_boundary(const BoundaryArgs& a, int D, hipStream_t s);
+
 // Draft prefill attention (bf16, D = 128): every raw query of a prefix and every slot
 // query, each under the memory of its own step.  One work-group per block of `qb`
 // consecutive queries of one (sequence, KV head); blocks [0, raw_blocks) hold raw

@@ -329,23 +329,49 @@ def rollback_leg(dev, reps=4):
     return dict(op="masw_rollback", us_per_layer=round(us, 2), rollback_rows=16, batch=sh.batch, checked=ok)
 
 
-def single_sequence_leg(dev, steps=64, warmup=10):
+def read_floor_us(dev, nbytes, n_bufs, reps=3):
+    """Per-launch time of the plain streaming-read kernel (masw_stream_read) at `nbytes`
+    per launch over `n_bufs` distinct buffers replayed in a graph, the fastest of 256 to
+    2048 work-groups: what a kernel that only reads can do at this launch size."""
+    total = torch.zeros(M.STREAM_SUMS, dtype=torch.int32, device=dev)
+    n16 = nbytes // 16 * 16
+    bufs = [torch.ones(n16 // 4, dtype=torch.int32, device=dev) for _ in range(n_bufs)]
+    us = min(graph_per_call_us(lambda i: M.stream_read(bufs[i % n_bufs], total, work_groups=wgs), 2 * n_bufs)
+             for wgs in (256, 512, 1024, 2048) for _ in range(reps))
+    del bufs
+    torch.cuda.empty_cache()
+    return round(us, 2), int(n16)
+
+
+def single_sequence_leg(dev, steps=32, warmup=6):
     """The batch-1 workload: one sequence at prefix 8192, K,V ~ 0.5 N(0,1), the MASW
-    memory holding the full cache's own raw rows; MASW and full-KV graph steps over the
-    same 28 layers."""
+    memory holding the full cache's own raw rows; MASW and full-KV graph steps.
+
+    Two sets of the 28 layers are allocated and every graph replay runs both in turn (56
+    distinct layers: 492 MB of MASW memory, 1.9 GB of full cache), so nothing is served
+    from the 256 MB last-level cache; the figures are per 28-layer step.  Next to them,
+    the streaming-read floor at each launch's size over the same number of buffers."""
     sh, t = SI.DRAFT_3B, SI.DRAFT_3B_PREFIX
-    st = Stack(sh, t + steps + warmup + 16, dev, seed=1)
+    sets = 2
+    st = Stack(dataclasses.replace(sh, layers=sets * sh.layers), t + steps + warmup + 16, dev, seed=1)
     st.capture()                   # its eager warm-up steps append into both caches
     st.mirror_full_into_masw(t)
     out = dict(workload="masw vs full-KV, 28 layers, batch 1, prefix 8192", prefix=t, batch=1,
-               keys_masw=keys_at(t, sh.sink, sh.window, sh.interval), keys_full=t)
+               keys_masw=keys_at(t, sh.sink, sh.window, sh.interval), keys_full=t,
+               layer_sets=sets, distinct_layers=st.L)
     for which in ("masw", "full"):
         ms, nb, q = time_steps(st, which, t, warmup, steps, quantiles=True)
+        ms, nb, q = ms / sets, nb / sets, tuple(round(x / sets, 4) for x in q)
         out[f"{which}_ms"] = round(ms, 4)
         out[f"{which}_ms_p10_p50_p90"] = q
         out[f"{which}_steps_per_s"] = round(1e3 / ms, 2)
         out[f"{which}_gbs"] = round(nb / (ms * 1e-3) / 1e9, 1)
         out[f"{which}_pct_peak"] = round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)
+        layer_bytes = nb / sh.layers
+        floor_us, floor_bytes = read_floor_us(dev, int(layer_bytes), st.L)
+        out[f"{which}_us_per_layer"] = round(ms * 1e3 / sh.layers, 2)
+        out[f"{which}_read_floor_us_per_layer"] = floor_us
+        out[f"{which}_over_read_floor"] = round(ms * 1e3 / sh.layers / floor_us, 2)
     out["full_over_masw_latency"] = round(out["full_ms"] / out["masw_ms"], 3)
     out["device_err_bits"] = int(st.seq.err.item()) | int(st.err_full.item())
     del st

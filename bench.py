@@ -731,30 +731,131 @@ def cpu_baseline(seconds=3.0, full_units=2):
 
 def profile_modes(args, dev):
     """Runs the dominant kernel alone, at the configuration of kernel_roofline."""
-    stack = Stack(SHAPE, T_HEAD + 64, dev, with_full=False)
+    stack = Stack(SHAPE, T_HEAD + 64, dev, with_full=args.traffic_probe)
     if args.roofline_only:
         roof = kernel_roofline(stack, T_HEAD)
         print(json.dumps({"roofline": roof, "source_sha256": decode_source_hash()}), flush=True)
         return
-    # --traffic-probe: 2 x 28 eager launches of the fused decode step, then a plain
-    # elementwise copy kernel over 256 MiB (torch.mul by 1 into another buffer, 4 launches)
-    # whose FETCH_SIZE / WRITE_SIZE calibrate the counters.
-    stack.set_position(T_HEAD)
+    counter_probe(stack, dev)
+
+
+def counter_probe(stack, dev):
+    """--traffic-probe: eager launches of every leg's kernels in a fixed order, for
+    rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE / matrix-core counters per dispatch).
+
+    Calibration first: 4 launches of a plain elementwise copy over 256 MiB (torch.mul by 1
+    into another buffer), whose FETCH_SIZE / WRITE_SIZE give the counters' scale, and 4
+    launches of masw_mfma_rate (register-operand MFMA chains) whose matrix-core busy
+    counter gives the busy figure of a saturated matrix core.  Then the legs, each a run
+    of `launches` dispatches of the kernel named in the printed manifest, in manifest
+    order; dispatches of other kernels (fills, input generation) come in between."""
+    sh = SHAPE
     L = stack.L
-    for i in range(2 * L):
-        M.masw_decode_step(stack.d, stack.layers[i % L], stack.seq, stack.k_new[i % L], stack.v_new[i % L],
-                           stack.q[i % L], stack.out[i % L], stack.ws)
-    torch.cuda.synchronize()
+    legs = []
     copy_bytes = 256 << 20
     src = torch.ones(copy_bytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(4):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    nbytes = stack.attn_bytes(keys_at(T_HEAD, stack.S, stack.W, stack.r)) + 2 * SHAPE.batch * stack.kv_row_bytes()
-    print(json.dumps({"decode_launches": 2 * L, "algorithmic_bytes_per_launch": int(nbytes),
-                      "copy_bytes_per_launch": copy_bytes, "copy_launches": 4,
-                      "source_sha256": decode_source_hash(), "err": int(stack.seq.err.item())}), flush=True)
+    del src, dst
+    mfma_wgs, mfma_iters = 256, 20000
+    mout = torch.empty(mfma_wgs * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    for _ in range(4):
+        M.mfma_rate(mfma_wgs, mfma_iters, mout, clocks)
+    torch.cuda.synchronize()
+    legs.append(dict(leg="mfma_rate", kernel="mfma_rate", launches=4,
+                     flops_per_launch=mfma_wgs * 4 * mfma_iters * 4 * 2 * 32 * 32 * 16))
+
+    # the dominant kernel: fused append + MASW attention, B=8, prefix 32768
+    stack.set_position(T_HEAD)
+    for i in range(2 * L):
+        M.masw_decode_step(stack.d, stack.layers[i % L], stack.seq, stack.k_new[i % L], stack.v_new[i % L],
+                           stack.q[i % L], stack.out[i % L], stack.ws)
+    torch.cuda.synchronize()
+    nbytes = stack.attn_bytes(keys_at(T_HEAD, stack.S, stack.W, stack.r)) + 2 * sh.batch * stack.kv_row_bytes()
+    legs.append(dict(leg="masw_decode_b8_t32768", kernel="decode_kernel", launches=2 * L,
+                     bytes_per_launch=int(nbytes)))
+
+    # full-KV fused append + attention at the same prefix (default plan)
+    stack.seq_full.fill_(T_HEAD)
+    for i in range(L):
+        M.fullkv_decode_step(stack.fd, stack.kf[i], stack.vf[i], stack.seq_full, stack.err_full,
+                             stack.k_new[i], stack.v_new[i], stack.q[i], stack.out[i], stack.ws_full)
+    torch.cuda.synchronize()
+    legs.append(dict(leg="fullkv_decode_b8_t32768", kernel="decode_kernel", launches=L,
+                     bytes_per_launch=int(stack.attn_bytes(T_HEAD) + 2 * sh.batch * stack.kv_row_bytes())))
+
+    # a slot boundary (projection + slot query in one launch) at B=8 and at B=4
+    t_b = first_boundary_after(T_HEAD + 64, stack.S, stack.W, stack.r)
+    m = (t_b - stack.S - stack.W) // stack.r
+    stack.set_position(t_b)
+    proj_bytes = 2 * sh.hidden * sh.n_kv_heads * sh.head_dim * 2
+    for B in (sh.batch, sh.batch // 2):
+        d = dataclasses.replace(stack.d, batch=B)
+        ws = M.workspace(d, M.OP_MATERIALIZE, device=dev)
+        seq = M.Seq(seq_len=stack.seq.seq_len[:B], err=stack.seq.err)
+        for i in range(L):
+            lay = stack.layers[i]
+            lay.n_slots.fill_(m - 1)
+            lb = M.Layer(**{f.name: getattr(lay, f.name)[:B] for f in dataclasses.fields(lay)})
+            M.masw_materialize_slot(d, lb, seq, stack.h[i][:B], stack.wk[i], stack.wv[i],
+                                    stack.qg[i][:B], stack.og[i][:B], ws)
+        torch.cuda.synchronize()
+        keys = stack.S + stack.W + m - 1
+        legs.append(dict(leg=f"boundary_b{B}_slot{m}", kernel="boundary_kernel", launches=L,
+                         bytes_per_launch=int(proj_bytes + B * sh.hidden * 2 + stack.attn_bytes(keys) * B // sh.batch
+                                              + B * stack.kv_row_bytes()),
+                         flops_per_launch=2 * B * sh.hidden * 2 * sh.n_kv_heads * sh.head_dim,
+                         mfma_rows_per_launch=-(-B // 16) * 16))
+        del ws
+    del stack
+    torch.cuda.empty_cache()
+
+    # the batch-1 workload at prefix 8192 (one layer set)
+    sh1, t1 = SI.DRAFT_3B, SI.DRAFT_3B_PREFIX
+    st = Stack(sh1, t1 + 64, dev, seed=1)
+    st.mirror_full_into_masw(t1)
+    st.set_position(t1)
+    for i in range(st.L):
+        M.masw_decode_step(st.d, st.layers[i], st.seq, st.k_new[i], st.v_new[i], st.q[i], st.out[i], st.ws)
+    for i in range(st.L):
+        M.fullkv_decode_step(st.fd, st.kf[i], st.vf[i], st.seq_full, st.err_full,
+                             st.k_new[i], st.v_new[i], st.q[i], st.out[i], st.ws_full)
+    torch.cuda.synchronize()
+    legs.append(dict(leg="masw_decode_b1_t8192", kernel="decode_kernel", launches=st.L,
+                     bytes_per_launch=int(st.attn_bytes(keys_at(t1, st.S, st.W, st.r)) + 2 * st.kv_row_bytes())))
+    legs.append(dict(leg="fullkv_decode_b1_t8192", kernel="decode_kernel", launches=st.L,
+                     bytes_per_launch=int(st.attn_bytes(t1) + 2 * st.kv_row_bytes())))
+    err = int(st.seq.err.item()) | int(st.err_full.item())
+    del st
+    torch.cuda.empty_cache()
+
+    # verifier layers (8B and 70B shapes, one GPU's 8 KV heads, batch 4, prefix 32768 + 6)
+    batch, n_q, t = 4, 6, 32768 + 6
+    for Hq in (32, 64):
+        vd = M.Dims(batch=batch, n_q_heads=Hq, n_kv_heads=8, head_dim=128, dtype=torch.bfloat16)
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        kv = [torch.randn(batch, 8, t + 8, 128, device=dev, dtype=torch.bfloat16, generator=g) for _ in range(4)]
+        vv = [torch.randn(batch, 8, t + 8, 128, device=dev, dtype=torch.bfloat16, generator=g) for _ in range(4)]
+        qv = torch.randn(batch, n_q, Hq, 128, device=dev, dtype=torch.bfloat16, generator=g)
+        ov = torch.empty_like(qv)
+        sv = torch.full((batch,), t, dtype=torch.int32, device=dev)
+        ev = torch.zeros(1, dtype=torch.int32, device=dev)
+        wsv = M.workspace(vd, M.OP_FULLKV_VERIFY, max_keys=t + 8, n_q=n_q, device=dev)
+        for i in range(8):
+            M.fullkv_verify_attn(vd, kv[i % 4], vv[i % 4], sv, ev, qv, ov, wsv)
+        torch.cuda.synchronize()
+        err |= int(ev.item())
+        legs.append(dict(leg=f"verify_{Hq}q8kv_b4_t32774", kernel="verify_stream_kernel", launches=8,
+                         bytes_per_launch=batch * (t * 8 * 128 * 2 * 2 + 2 * n_q * Hq * 128 * 2),
+                         flops_per_launch=4 * batch * n_q * Hq * 128 * t))
+        del kv, vv
+        torch.cuda.empty_cache()
+    print(json.dumps({"copy_bytes_per_launch": copy_bytes, "copy_launches": 4, "legs": legs,
+                      "source_sha256": decode_source_hash(), "err": err}), flush=True)
 
 
 def main():
@@ -770,7 +871,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the draft prefill leg (for rocprofv3 --kernel-trace --stats)")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="eager launches of the dominant kernel and a 256 MiB copy (for rocprofv3 --pmc)")
+                    help="eager launches of every leg's kernels after copy and matrix-core "
+                         "calibration kernels (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the draft path shards by sequence or KV head "

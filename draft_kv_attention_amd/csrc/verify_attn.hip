@@ -30,6 +30,7 @@ constexpr int kVThreads = kVWaves * kWave;
 constexpr int kRS = 136;       // LDS row stride of the staged queries in bf16 elements (272 bytes)
 constexpr int kD = 128;
 constexpr int kMaxRows = 64;
+constexpr float kVLazyMax = 8.f;   // log2 units a row's reference max may trail its true max
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -59,6 +60,21 @@ constexpr int kVSplitRound = kVWaves * kVWaveKeys;    // keys per split rounding
 __device__ __forceinline__ void verify_issue(u32x4_t* stage, const uint16_t* kbase, const uint16_t* vbase, int tile,
                                              int k1, int lane) {
   const int sub = lane >> 4, slot = lane & 15;
+  if (tile + kVWaveKeys <= k1) {
+    // a whole tile: one wave-uniform base plus a per-lane constant per copy
+    const uint16_t* kt = kbase + size_t(tile) * kD;
+    const uint16_t* vt = vbase + size_t(tile) * kD;
+#pragma unroll
+    for (int q = 0; q < kVWaveKeys / 4; ++q) {
+      const int row = 4 * q + sub;
+      const int off = row * kD + ((slot ^ tile_swz(row)) << 3);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kt + off), (lds_ptr_t)(stage + q * kWave), 16, 0,
+                                       kStreamLoadNT);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vt + off),
+                                       (lds_ptr_t)(stage + (kVWaveKeys / 4 + q) * kWave), 16, 0, kStreamLoadNT);
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < kVWaveKeys / 4; ++q) {
     const int row = 4 * q + sub;
@@ -225,36 +241,38 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
     for (int rb = 0; rb < NB; ++rb) {
       f32x16_t s = sacc[rb];
       // S^T layout: register v holds key 8*(v/4) + 4*half + v%4 of the tile, row l32.
-      // Tiles below every row's causal limit and inside the range need no mask.
+      // Tiles below every row's causal limit and inside the range need no mask.  The
+      // raw scores' max is taken first (the scale is positive) and the scale goes into
+      // the exponent's FMA.
       float tmax = -INFINITY;
       if (interior) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[v] *= a.scale_log2;
-          tmax = fmaxf(tmax, s[v]);
-        }
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = tile + 8 * (v >> 2) + 4 * half + (v & 3);
-          const float sc = (key < w1 && key <= lim[rb]) ? s[v] * a.scale_log2 : -INFINITY;
-          s[v] = sc;
-          tmax = fmaxf(tmax, sc);
+          s[v] = (key < w1 && key <= lim[rb]) ? s[v] : -INFINITY;
+          tmax = fmaxf(tmax, s[v]);
         }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float mn = fmaxf(m[rb], tmax);
-      const float mref = mn == -INFINITY ? 0.f : mn;   // a row may have no key in this tile
-      const float alpha = fast_exp2(m[rb] - mref);
-      if (__any(mn != m[rb])) {   // rescale only when some row's max grew
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * a.scale_log2;   // log2 units; -inf: no key
+      // m is the row's reference max, raised only when the tile's max passes it by more
+      // than kVLazyMax: the weights stay below 2^kVLazyMax and the rescale of l and o -
+      // with many rows per wave it would otherwise run on almost every tile - becomes rare.
+      // The result is the same softmax: (m, l, o) stay consistent, whatever m is.
+      const bool grow = tmax > m[rb] + kVLazyMax;
+      if (__any(grow)) {
+        const float alpha = grow ? fast_exp2(m[rb] - tmax) : 1.f;
         l[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
+        m[rb] = grow ? tmax : m[rb];
       }
-      m[rb] = mn;
+      const float mref = m[rb] == -INFINITY ? 0.f : m[rb];   // a row may have no key yet
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(s[v] - mref);
+        const float p = fast_exp2(fmaf(s[v], a.scale_log2, -mref));
         s[v] = p;
         l[rb] += p;
       }

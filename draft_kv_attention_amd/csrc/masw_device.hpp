@@ -113,13 +113,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // part a device-scope __threadfence() writes back and invalidates the whole L2 of the
 // issuing XCD, which costs far more than the partials themselves, so partials are
 // written and read with agent-scope relaxed atomics (per-access write-through /
-// L2-bypassing, coherent across XCDs).  Two protocols use them:
-//  - ticket after data (the projection's hidden slices): every work-group stores its
-//    partial, waits for the stores (s_waitcnt vmcnt(0)), then takes a ticket
-//    (split_arrive); the last arrival loads the others' partials;
-//  - self-validating partials (the decode kernel, decode_attn.hip): partials are stored
-//    encoded so that an unwritten (zero) slot is recognisable and the ticket need not
-//    wait for the data.
+// L2-bypassing, coherent across XCDs).  Every work-group stores its partial, waits for
+// the stores (s_waitcnt vmcnt(0)), then takes a ticket (split_arrive); the last arrival
+// loads the others' partials and resets the ticket.  The decode kernel's split merge and
+// the projection's hidden slices both work this way.
 
 __device__ __forceinline__ void store_partial(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

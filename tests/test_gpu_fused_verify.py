@@ -115,11 +115,14 @@ def _verify_case(B, Hq, Hkv, D, n_q, ts, max_len, dtype, seed, check_b=None, spl
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     scale = O.default_scale(D)
+    got_all, ref_all = [], []
     for b in (check_b if check_b is not None else range(B)):
         kn, vn = np_in(k[b]), np_in(v[b])
         ref = O.fullkv_verify(np_in(q[b]).astype(np.float64), kn, vn, ts[b], scale)
         assert_close(out[b], ref, dtype, f"verify b={b} t={ts[b]}")
-    return out
+        got_all.append(np_in(out[b]).astype(np.float64).ravel())
+        ref_all.append(np.asarray(ref, np.float64).ravel())
+    return out, np.concatenate(got_all), np.concatenate(ref_all)
 
 
 @pytest.mark.parametrize("Hq", [32, 64])
@@ -127,8 +130,15 @@ def test_verify_full_size(Hq):
     """One GPU's share of an 8B / 70B verifier layer: 8 KV heads, prefix 32768 + 6."""
     sh = SI.VERIFY_8B if Hq == 32 else SI.VERIFY_70B
     t = sh.prefix + sh.n_query
-    _verify_case(sh.batch, sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.n_query, [t] * sh.batch,
-                 t + 10, torch.bfloat16, seed=31, check_b=[0, sh.batch - 1])
+    _, got, ref = _verify_case(sh.batch, sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.n_query, [t] * sh.batch,
+                               t + 10, torch.bfloat16, seed=31, check_b=[0, sh.batch - 1])
+    # error budget of the bf16 path (P rounded to bf16 for P.V, fp32 accumulation, a bf16
+    # output) against the rounding of the exact output alone
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    rel_round = np.linalg.norm(O.to_bf16(ref) - ref) / np.linalg.norm(ref)
+    print(f"verifier {Hq}q: rel-L2 {rel:.3e} (bf16 rounding of the exact output alone: {rel_round:.3e}), "
+          f"max abs {np.abs(got - ref).max():.3e}")
+    assert rel <= 2.0 * rel_round, (rel, rel_round)
 
 
 @pytest.mark.parametrize("Hq,Hkv,n_q", [(24, 8, 6), (32, 8, 6), (64, 8, 6), (8, 8, 1), (32, 8, 16),

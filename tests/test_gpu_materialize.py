@@ -107,6 +107,7 @@ def test_bench_launch_configuration_sampled_rows():
     kn, vn = np_in(st.k_new[1]), np_in(st.v_new[1])
     q = np_in(st.q[1]).astype(np.float64)
     G = sh.group
+    got_all, ref_all = [], []
     for b in (0, 3, 7):
         for kvh in (0, 5):
             K = np.empty((len(keys), sh.head_dim))
@@ -122,6 +123,16 @@ def test_bench_launch_configuration_sampled_rows():
                 h = kvh * G + g
                 ref = O.attend(q[b, h], K, V, st.d.softmax_scale)
                 assert_close(st.out[1][b, h], ref, torch.bfloat16, f"b={b} h={h}")
+                got_all.append(np_in(st.out[1][b, h]).astype(np.float64))
+                ref_all.append(ref)
+    # Error budget of the bf16 path (P rounded to bf16 for the P.V product, fp32
+    # accumulation, a bf16 output): against the rounding of the exact output alone.
+    got_all, ref_all = np.concatenate(got_all), np.concatenate(ref_all)
+    rel = np.linalg.norm(got_all - ref_all) / np.linalg.norm(ref_all)
+    rel_round = np.linalg.norm(O.to_bf16(ref_all) - ref_all) / np.linalg.norm(ref_all)
+    print(f"headline decode launch: rel-L2 {rel:.3e} (bf16 rounding of the exact output alone: {rel_round:.3e}), "
+          f"max abs {np.abs(got_all - ref_all).max():.3e}")
+    assert rel <= 2.0 * rel_round, (rel, rel_round)
     # the new token landed in its ring row
     c = O.ring_cell(t, S, W, r)
     assert torch.equal(lay.k_ring[:, :, c], st.k_new[1][:, 0])

@@ -179,3 +179,56 @@ def test_projection_hidden_splits_and_batch_groups(hidden, B):
         assert torch.isfinite(o.float()).all()
         rows.append((layer.k_slot[:, :, 0].clone(), layer.v_slot[:, :, 0].clone()))
     assert torch.equal(rows[0][0], rows[1][0]) and torch.equal(rows[0][1], rows[1][1])
+
+
+def test_boundary_launch_graph_replay_matches_eager():
+    """The one-launch boundary (projection + gated slot query, bf16) captured in a HIP
+    graph and replayed four times, with eager work in between (the layer reset to slot
+    m - 1): every replay leaves the same slot rows, outputs and n_slots as the eager
+    call, bit for bit, so the launch's tickets are back at zero after every call.
+    Sequence 2 already holds slot m and is left untouched."""
+    import dataclasses
+    import bench
+    shape = dataclasses.replace(SI.SWEEP_3B, layers=1, batch=4)
+    S, W, r = shape.sink, shape.window, shape.interval
+    t_b = bench.first_boundary_after(4000, S, W, r)
+    m = (t_b - S - W) // r
+    st = bench.Stack(shape, t_b + 64, torch.device(DEV), seed=5, with_full=False)
+    st.set_position(t_b)
+    lay = st.layers[0]
+    have = torch.tensor([m - 1, m - 1, m, m - 1], dtype=torch.int32, device=DEV)
+    ks0, vs0 = lay.k_slot.clone(), lay.v_slot.clone()
+
+    def reset():
+        lay.n_slots.copy_(have)
+        lay.k_slot.copy_(ks0)
+        lay.v_slot.copy_(vs0)
+        st.og[0].fill_(float("nan"))
+
+    def call():
+        M.masw_materialize_slot(st.d, lay, st.seq, st.h[0], st.wk[0], st.wv[0], st.qg[0], st.og[0], st.ws)
+
+    reset()
+    call()
+    torch.cuda.synchronize()
+    assert int(st.seq.err.item()) == 0
+    eager = [lay.k_slot.clone(), lay.v_slot.clone(), st.og[0].clone(), lay.n_slots.clone()]
+    assert lay.n_slots.tolist() == [m, m, m, m]
+    assert torch.equal(lay.k_slot[2], ks0[2]) and torch.isnan(st.og[0][2].float()).all()
+    assert not torch.equal(lay.k_slot[0, :, m - 1], ks0[0, :, m - 1])
+    reset()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        reset()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [lay.k_slot, lay.v_slot, st.og[0], lay.n_slots]
+        for name, a_, b_ in zip(("k_slot", "v_slot", "og", "n_slots"), got, eager):
+            assert torch.equal(torch.nan_to_num(a_.float(), 7.0), torch.nan_to_num(b_.float(), 7.0)), f"replay {i} {name}"
+    assert int(st.seq.err.item()) == 0

@@ -140,7 +140,7 @@ struct VerifyArgs {
 
 int launch_verify_mfma(const VerifyArgs& a, hipStream_t s);
 constexpr int kMaxVerifySplits = 64;   // splits the MFMA verifier merges (more are clamped)
-// Verifier work-groups resident per CU: the streaming kernel holds 128-150 KB of LDS.
+// Verifier work-groups resident per CU: the streaming kernel holds ~132 KB of LDS.
 inline int verify_resident_per_cu(int /*rows*/) { return 1; }
 
 }  // namespace masw

@@ -27,7 +27,6 @@ namespace {
 
 constexpr int kVWaves = 4;
 constexpr int kVThreads = kVWaves * kWave;
-constexpr int kRS = 136;       // LDS row stride of the staged queries in bf16 elements (272 bytes)
 constexpr int kD = 128;
 constexpr int kMaxRows = 64;
 constexpr float kVLazyMax = 8.f;   // log2 units a row's reference max may trail its true max
@@ -106,32 +105,20 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
   __shared__ float sm_ml[kVWaves][NB * 32][2];
 
   const int t = a.seq_len[b];
-  // Q^T operand (B of S^T = K Q^T): lane holds row rb*32 + l32, d = 16 ks + 8 half .. +7.
-  // One row block keeps it in registers; two read it from padded LDS rows per step
-  // (registers would not hold both blocks' accumulators and fragments).
-  constexpr bool kQRegs = NB == 1;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kQRegs ? 8 : NB * 32 * kRS];
-  u32x4_t bq[kQRegs ? 8 : 1];
-  if constexpr (kQRegs) {
-    const int row = l32;
+  // Q^T operand (B of S^T = K Q^T): lane holds row rb*32 + l32, d = 16 ks + 8 half .. +7,
+  // in registers for every row block (with one wave per SIMD the two blocks' operands,
+  // accumulators and fragments fit in its 512 registers; reading the second block's Q
+  // from LDS every tile measured ~1 us slower per 70B-shaped layer).
+  u32x4_t bq[NB][8];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int row = rb * 32 + l32;
     const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            ((size_t(b) * a.n_q + (row < R ? j : 0)) * a.Hq + size_t(kvh) * G + (row < R ? g : 0)) * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      bq[ks] = row < R ? *reinterpret_cast<const u32x4_t*>(qrow + ks * 16 + half * 8) : u32x4_t{0, 0, 0, 0};
-  } else {
-    for (int c = threadIdx.x; c < NB * 32 * 16; c += kVThreads) {
-      const int row = c >> 4, ch = c & 15;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (row < R) {
-        const int g = row / a.n_q, j = row - (row / a.n_q) * a.n_q;
-        v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) +
-                                              ((size_t(b) * a.n_q + j) * a.Hq + size_t(kvh) * G + g) * kD + ch * 8);
-      }
-      *reinterpret_cast<u32x4_t*>(sQ + row * kRS + ch * 8) = v;
-    }
-    __syncthreads();
+      bq[rb][ks] = row < R ? *reinterpret_cast<const u32x4_t*>(qrow + ks * 16 + half * 8) : u32x4_t{0, 0, 0, 0};
   }
   if (t < a.n_q || t > a.max_len) {
     if (split == 0 && kvh == 0 && threadIdx.x == 0) atomicOr(a.err, MASW_DEV_SEQ_RANGE);
@@ -230,9 +217,7 @@ __global__ __launch_bounds__(kVThreads) void verify_stream_kernel(const VerifyAr
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
-        u32x4_t qf;
-        if constexpr (kQRegs) qf = bq[ks];
-        else qf = *reinterpret_cast<const u32x4_t*>(sQ + (rb * 32 + l32) * kRS + ks * 16 + half * 8);
+        const u32x4_t qf = bq[rb][ks];
         sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
                                                            __builtin_bit_cast(bf16x8_t, qf), sacc[rb], 0, 0, 0);
       }

@@ -141,6 +141,39 @@ def test_verify_full_size(Hq):
     assert rel <= 2.0 * rel_round, (rel, rel_round)
 
 
+@pytest.mark.parametrize("Hq", [32, 64])
+def test_verify_score_growth_restarts(Hq):
+    """Keys whose scores pass everything seen before by 200-400 log2 units, in later tiles
+    of a wave's range (two of them in one wave): weights taken against a reference max set
+    by the first tiles would overflow fp32, so the kernel must raise it on the way (and
+    rescale what it has accumulated) to match the oracle."""
+    B, Hkv, D, n_q, t, splits = 2, 8, 128, 6, 5000, 16
+    G = Hq // Hkv
+    k, v = SI.full_cache(B, Hkv, t + 8, D, seed=41, dtype=torch.bfloat16)
+    q = SI.normal((B, n_q, Hq, D), 42, dtype=torch.bfloat16)
+    scale = O.default_scale(D)
+    qh = q[0, 0, 3 * G].double()
+    # 16 splits asked for: chunks of 384 keys (96 per wave, tiles of 32), so keys 1876 /
+    # 1910 are tiles 1 / 2 of split 4's last wave and 4200 is tile 2 of split 10's
+    for pos, target in ((1876, 200.0), (1910, 400.0), (4200, 300.0)):
+        kk = qh * (target / (scale * np.log2(np.e)) / float(qh @ qh))
+        k[0, 3, pos] = kk.to(torch.bfloat16)
+    d = M.Dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, dtype=torch.bfloat16, num_splits=splits)
+    kd, vd, qd = k.to(DEV), v.to(DEV), q.to(DEV)
+    seq = torch.full((B,), t, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.full_like(qd, float("nan"))
+    M.fullkv_verify_attn(d, kd, vd, seq, err, qd, out, M.workspace(d, M.OP_FULLKV_VERIFY, max_keys=t + 8, n_q=n_q,
+                                                                   device=DEV))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for b in range(B):
+        ref = O.fullkv_verify(np_in(q[b]).astype(np.float64), np_in(k[b]), np_in(v[b]), t, scale)
+        assert_close(out[b], ref, torch.bfloat16, f"verify b={b}")
+    # the key planted last dominates candidate 0 of head 3G: its output is that value row
+    assert torch.allclose(out[0, 0, 3 * G].float().cpu(), v[0, 3, 1910].float(), atol=2e-2)
+
+
 @pytest.mark.parametrize("Hq,Hkv,n_q", [(24, 8, 6), (32, 8, 6), (64, 8, 6), (8, 8, 1), (32, 8, 16),
                                         (64, 8, 8), (24, 8, 2)])
 def test_verify_ragged_small(Hq, Hkv, n_q):

@@ -632,7 +632,8 @@ def materialize_leg(stack, t_boundary, replays=5, dims=None, ws=None):
     nbytes = (2 * sh.hidden * sh.n_kv_heads * sh.head_dim * 2 + B * sh.hidden * 2
               + stack.attn_bytes(keys) * B // sh.batch + B * stack.kv_row_bytes())
     return dict(batch=B, slot_index=m, us_per_layer=round(per_layer, 2), bytes_per_layer=int(nbytes),
-                gbs=round(nbytes / per_layer / 1e3, 1), per_decode_step_us=round(per_layer * L / stack.r, 2),
+                gbs=round(nbytes / per_layer / 1e3, 1), pct_peak=round(100 * nbytes / per_layer / 1e3 / HBM_PEAK_GBS, 1),
+                boundaries_per_s=round(1e6 / (per_layer * L), 1), per_decode_step_us=round(per_layer * L / stack.r, 2),
                 slots_after=int(stack.layers[0].n_slots[0].item()), device_err_bits=int(seq.err.item()))
 
 

@@ -752,6 +752,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 // both run side by side - each sequence gated by its own boundary decision.  Every
 // work-group reads n_slots at its start; the last one to finish (a launch-wide ticket)
 // publishes n_slots = m for the sequences at their boundary and resets the ticket.
+// Thread b of every work-group takes sequence b's decision together with its other
+// start-up loads (nothing is published before every work-group has arrived, so it is
+// the decision the gates saw), and the last work-group stores it without another load.
 template <int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void boundary_kernel(const BoundaryArgs a) {
   __shared__ union {
@@ -760,6 +763,12 @@ __global__ __launch_bounds__(kDecodeThreads) void boundary_kernel(const Boundary
   } lds;
   __shared__ int sm_done;
   const int id = blockIdx.x;
+  const bool mine = int(threadIdx.x) < a.d.B;
+  int own_t = 0, own_have = 0;
+  if (mine) {
+    own_t = a.d.seq_len[threadIdx.x];
+    own_have = a.d.n_slots[threadIdx.x];
+  }
   if (id < a.n_proj) {
     proj::project_mfma_body<1>(a.p, id % a.proj_x, (id / a.proj_x) % 2, id / (2 * a.proj_x), lds.p);
   } else {
@@ -771,7 +780,11 @@ __global__ __launch_bounds__(kDecodeThreads) void boundary_kernel(const Boundary
     sm_done = __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.n_wg - 1;
   __syncthreads();
   if (!sm_done) return;
-  for (int b = threadIdx.x; b < a.d.B; b += kDecodeThreads) {
+  if (mine) {
+    const int m = pending_slot(own_t, own_have, a.d.g);
+    if (m) a.publish[threadIdx.x] = m;
+  }
+  for (int b = threadIdx.x + kDecodeThreads; b < a.d.B; b += kDecodeThreads) {
     const int m = pending_slot(a.d.seq_len[b], a.d.n_slots[b], a.d.g);
     if (m) a.publish[b] = m;
   }

@@ -175,8 +175,10 @@ def test_verify_score_growth_restarts(Hq):
 
 
 @pytest.mark.parametrize("Hq,Hkv,n_q", [(24, 8, 6), (32, 8, 6), (64, 8, 6), (8, 8, 1), (32, 8, 16),
-                                        (64, 8, 8), (24, 8, 2)])
+                                        (64, 8, 8), (24, 8, 2), (24, 8, 11), (24, 8, 12), (32, 8, 9)])
 def test_verify_ragged_small(Hq, Hkv, n_q):
+    """Rows per (sequence, KV head) R = G n_q of 6 to 64: one or two 32-row blocks, or three
+    16-row blocks for R in (32, 48] (33, 36 and 36 rows with padded tails, and 48)."""
     ts = [n_q, n_q + 1, 31, 33, 100, 1000, 3000]
     _verify_case(len(ts), Hq, Hkv, 128, n_q, ts, 3100, torch.bfloat16, seed=32)
 
@@ -189,7 +191,7 @@ def test_verify_vector_alu_shapes(dtype, D, Hq, n_q):
 
 
 @pytest.mark.parametrize("splits", [3, 12, 33, 64])
-@pytest.mark.parametrize("Hq,n_q", [(32, 6), (64, 8)])
+@pytest.mark.parametrize("Hq,n_q", [(32, 6), (64, 6), (64, 8)])
 def test_verify_split_plans(splits, Hq, n_q):
     """Split plans whose combine pass folds more than one batch of eight partials (up to
     the MFMA verifier's 64), with causal rows whose last splits see no key."""

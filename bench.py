@@ -850,7 +850,7 @@ def counter_probe(stack, dev):
             M.fullkv_verify_attn(vd, kv[i % 4], vv[i % 4], sv, ev, qv, ov, wsv)
         torch.cuda.synchronize()
         err |= int(ev.item())
-        legs.append(dict(leg=f"verify_{Hq}q8kv_b4_t32774", kernel="verify_stream_kernel", launches=8,
+        legs.append(dict(leg=f"verify_{Hq}q8kv_b4_t32774", kernel="verify_stream", launches=8,
                          bytes_per_launch=batch * (t * 8 * 128 * 2 * 2 + 2 * n_q * Hq * 128 * 2),
                          flops_per_launch=4 * batch * n_q * Hq * 128 * t))
         del kv, vv

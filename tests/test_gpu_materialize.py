@@ -232,3 +232,55 @@ def test_boundary_launch_graph_replay_matches_eager():
         for name, a_, b_ in zip(("k_slot", "v_slot", "og", "n_slots"), got, eager):
             assert torch.equal(torch.nan_to_num(a_.float(), 7.0), torch.nan_to_num(b_.float(), 7.0)), f"replay {i} {name}"
     assert int(st.seq.err.item()) == 0
+
+
+def test_boundary_launch_more_sequences_than_threads():
+    """The one-launch boundary (bf16) with 300 sequences, more than a work-group has
+    threads: thread b of each work-group takes sequence b's boundary decision at start-up
+    and the rest are decided again by the last work-group.  A third of the sequences are
+    at their first boundary (projected and queried, n_slots -> 1), a third already hold
+    that slot and a third are one step past the boundary (both left untouched: slot rows
+    and outputs stay NaN, n_slots unchanged), in every range of sequence indexes."""
+    B, Hq, Hkv, D, S, W, r, hidden = 300, 2, 1, 64, 2, 8, 4, 64
+    d = M.Dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, sink=S, window=W, interval=r,
+               max_slots=4, dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(77)
+    wk = (torch.randn(hidden, Hkv * D, generator=g) * 0.05).to(torch.bfloat16)
+    wv = (torch.randn(hidden, Hkv * D, generator=g) * 0.05).to(torch.bfloat16)
+    h = torch.randn(B, hidden, generator=g).to(torch.bfloat16)
+    qg = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    t1 = S + W + r
+    k = torch.randn(B, t1, Hkv, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, t1, Hkv, D, generator=g).to(torch.bfloat16)
+    layer = M.alloc_layer(d, DEV, fill=float("nan"))
+    layer.n_slots.zero_()
+    seq = M.alloc_seq(B, DEV)
+    ws = M.workspace(d, M.OP_MATERIALIZE, device=DEV)
+    seq.seq_len.fill_(t1)
+    M.masw_evict_append(d, layer, seq, k.to(DEV), v.to(DEV))
+    cls = torch.arange(B) % 3                     # 0: pending, 1: already done, 2: past the boundary
+    layer.n_slots.copy_((cls == 1).to(torch.int32).to(DEV))
+    seq.seq_len.copy_(torch.where(cls == 2, t1 + 1, t1).to(torch.int32).to(DEV))
+    o = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    M.masw_materialize_slot(d, layer, seq, h.to(DEV), wk.to(DEV), wv.to(DEV), qg.to(DEV), o, ws)
+    torch.cuda.synchronize()
+    assert int(seq.err.item()) == 0
+    assert layer.n_slots.cpu().tolist() == [1 if c < 2 else 0 for c in cls.tolist()]
+    kg, vg = O.project_slot(np_in(h).astype(np.float64), np_in(wk).astype(np.float64),
+                            np_in(wv).astype(np.float64), Hkv, D, bf16_cache=True)
+    hn = np_in(h).astype(np.float64)
+    on = (cls == 0).numpy()
+    got_k = layer.k_slot[:, :, 0].double().cpu().numpy()
+    got_v = layer.v_slot[:, :, 0].double().cpu().numpy()
+    assert_slot_close(got_k[on], kg[on], slot_bound(hn[on], np_in(wk).astype(np.float64), Hkv, D), "slot K")
+    assert_slot_close(got_v[on], vg[on], slot_bound(hn[on], np_in(wv).astype(np.float64), Hkv, D), "slot V")
+    assert np.isnan(got_k[~on]).all() and np.isnan(got_v[~on]).all()
+    assert torch.isnan(o[torch.from_numpy(~on).to(DEV)].float()).all()
+    kn, vn, qn = np_in(k), np_in(v), np_in(qg).astype(np.float64)
+    idx = np.flatnonzero(on)
+    ref = []
+    for b in idx:
+        mem = O.DraftMemory(S, W, r, Hkv, D, bf16_cache=True)
+        mem.append(kn[b], vn[b])
+        ref.append(mem.slot_query(1, qn[b], d.softmax_scale))
+    assert_close(o[torch.from_numpy(idx).to(DEV)], np.stack(ref), torch.bfloat16, "slot query, 100 sequences")

@@ -1,10 +1,11 @@
 // append.hip - raw-token append with implicit eviction (Technical Review §3.2,
 // Algorithm 1 step 5; §3.1 Eq. 4 local bullet).
 //
-// Position i <= S lands in sink row i-1; i > S in ring row (i-S-1) mod (W+r).  The
-// ring keeps W + r rows because a block leaves the W-window r-1 steps before its slot
-// is materialized and the slot query still reads it; overwriting a row therefore
-// evicts the token i-(W+r), which is legal only once that token's block has its slot.
+// Position i <= S lands in sink row i-1; i > S in ring row (i-S-1) mod C, C = W + r
+// plus the rollback rows.  The ring keeps at least W + r rows because a block leaves
+// the W-window r-1 steps before its slot is materialized and the slot query still reads
+// it (the rollback rows keep speculative appends undoable); overwriting a row therefore
+// evicts the token i-C, which is legal only once that token's block has its slot.
 // Each thread moves one 16-byte packet of K and of V; all packets of one token take
 // the same decision (append_fate), so an illegal token is skipped whole, and so is a
 // token a later position of the same call overwrites.  A prefill append takes a whole

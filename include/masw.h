@@ -163,10 +163,10 @@ enum {
 
 /* Raw append with implicit eviction ([TR] §3.2 Algorithm 1 step 5; Eq. 4 local bullet).
  * k_new, v_new [B][n_new][Hkv][D] hold positions t-n_new+1 .. t (t = seq_len[b]).
- * Position i <= S goes to sink cell i-1; i > S to ring cell (i-S-1) mod (W+r), which
- * evicts the token i-(W+r) that occupied it.  That eviction is legal only if the
- * evicted token is a never-written cell or its block's slot already exists
- * (n_slots[b] >= ceil((i-(W+r)-S)/r)); otherwise the token is not written and
+ * Position i <= S goes to sink cell i-1; i > S to ring cell (i-S-1) mod C
+ * (C = W + r + rollback), which evicts the token i-C that occupied it.  That eviction is
+ * legal only if the evicted token is a never-written cell or its block's slot already
+ * exists (n_slots[b] >= ceil((i-C-S)/r)); otherwise the token is not written and
  * MASW_DEV_PENDING_SLOT is set.  Without a slot chain (r = 0) every eviction is legal.
  * t < n_new sets MASW_DEV_SEQ_RANGE and writes nothing.  n_new == 0 is a no-op. */
 MASW_API int masw_evict_append(const masw_dims* dims, const masw_layer* layer,

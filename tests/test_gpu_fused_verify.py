@@ -175,10 +175,12 @@ def test_verify_score_growth_restarts(Hq):
 
 
 @pytest.mark.parametrize("Hq,Hkv,n_q", [(24, 8, 6), (32, 8, 6), (64, 8, 6), (8, 8, 1), (32, 8, 16),
-                                        (64, 8, 8), (24, 8, 2), (24, 8, 11), (24, 8, 12), (32, 8, 9)])
+                                        (64, 8, 8), (24, 8, 2), (24, 8, 11), (24, 8, 12), (32, 8, 9),
+                                        (24, 8, 16)])
 def test_verify_ragged_small(Hq, Hkv, n_q):
     """Rows per (sequence, KV head) R = G n_q of 6 to 64: one or two 32-row blocks, or three
-    16-row blocks for R in (32, 48] (33, 36 and 36 rows with padded tails, and 48)."""
+    16-row blocks for R in (32, 48] (33, 36 and 36 rows with padded tails, and 48 rows as
+    8 heads x 6 candidates or 3 heads x 16)."""
     ts = [n_q, n_q + 1, 31, 33, 100, 1000, 3000]
     _verify_case(len(ts), Hq, Hkv, 128, n_q, ts, 3100, torch.bfloat16, seed=32)
 
